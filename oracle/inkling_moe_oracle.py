@@ -1,0 +1,244 @@
+"""Plain fp64 CPU oracle of the Inkling MoE feed-forward.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import or call this module.  It shares no code
+with the HIP library and imports nothing from it; inputs reach both sides from
+mixture_experts_feed_amd/workloads.py, which draws random numbers only.
+
+What it computes follows the Inkling layers page
+(nemo_automodel.components.models.inkling.layers):
+
+  * InklingGate: logits of the hidden states against a gate bank of n_routed
+    routed rows plus n_shared shared rows (fp32 gate precision); selection by
+    sigmoid(logit) + InklingCorrectionBias; returned weights = softmax of
+    log-sigmoid over [selected routed logits || shared logits], times
+    route_scale * global_scale.
+  * inkling_swiglu: SwiGLU on the interleaved [g0, u0, g1, u1, ...] layout,
+    the activated output scaled by the routing weight.
+  * InklingSharedExperts: always-on experts whose outputs are weighted by the
+    shared gammas before summation.
+  * InklingMoE.forward: routed + shared outputs summed, output shaped like the
+    input; padded tokens are excluded from routed dispatch.
+
+Everything runs in float64 on the exact input values (bf16 and fp32 inputs widen
+to fp64 without error, and their pairwise products are exact in fp64), with
+numpy's matmul, argsort and cumsum as the only library steps.  Readings taken
+where the pages are silent (documented in the design doc):
+  * gate-bank row order: routed rows 0..E-1, shared rows E..E+S-1;
+  * top-k order: descending biased score, equal scores -> lower expert index;
+  * route_scale * global_scale scales the shared gammas too;
+  * SwiGLU is silu(gate) * up with no clamp (hidden_act 'silu' on the
+    configuration page, InklingTextConfig);
+  * no normalisation of the hidden states inside the gate;
+  * padded tokens still pass through the shared experts.
+
+Pins (tests/test_oracle_pins.py, all CPU): brute-force top-k over every subset
+on tiny inputs, forced exact ties, the closed form sigma/sum(sigma) of the
+log-sigmoid softmax, gammas summing to route_scale*global_scale, the
+interleaved SwiGLU against the de-interleaved textbook form, a one-expert top-1
+MoE against a dense SwiGLU MLP, token independence, expert relabelling, and a
+hand-derived worked example (tests/golden/hand_example.json).  Agreement with
+the HuggingFace InklingTopkRouter or a real checkpoint: parity unpinned (neither
+exists here).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+# --------------------------------------------------------------------------
+# InklingGate (layers page, InklingGate; InklingCorrectionBias)
+# --------------------------------------------------------------------------
+
+def gate_logits(x, gate_bank) -> np.ndarray:
+    """z[t, j] = sum_h x[t, h] * bank[j, h]; rows j < E routed, E <= j shared.
+
+    InklingGate: the weight bank holds the routed rows plus n_shared_experts
+    rows; gate_precision defaults to float32, i.e. fp32 operands.  Here the sum
+    is taken in fp64 over exactly widened operands.
+    """
+    return _f64(x) @ _f64(gate_bank).T
+
+
+def sigmoid(z) -> np.ndarray:
+    """sigma(z) = 1 / (1 + exp(-z))."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def log_sigmoid(z) -> np.ndarray:
+    """log sigma(z) = -log(1 + exp(-z)), written for both signs of z without overflow."""
+    z = _f64(z)
+    return np.where(z >= 0, -np.log1p(np.exp(-np.abs(z))), z - np.log1p(np.exp(-np.abs(z))))
+
+
+def selection_scores(z_routed, bias) -> np.ndarray:
+    """s[t, e] = sigma(z[t, e]) + b[e]  (InklingGate: sigmoid scores plus a
+    per-expert correction bias; InklingCorrectionBias.forward adds it in the
+    routing score dtype, fp64 here)."""
+    return sigmoid(z_routed) + _f64(bias)[None, :]
+
+
+def topk_select(scores, k: int) -> np.ndarray:
+    """Indices [T, k] of the k largest scores per row, in descending score order,
+    equal scores ordered by lower expert index (InklingGate.top_k =
+    num_experts_per_tok; the tie rule is the reading taken here).
+
+    A stable argsort of -s keeps equal keys in ascending index order.
+    """
+    s = _f64(scores)
+    order = np.argsort(-s, axis=1, kind="stable")
+    return order[:, :k]
+
+
+def softmax(v, axis=-1) -> np.ndarray:
+    v = _f64(v)
+    m = np.max(v, axis=axis, keepdims=True)
+    e = np.exp(v - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def route(z, bias, n_routed: int, top_k: int, route_scale: float, global_scale: float):
+    """InklingGate.forward from the logits.
+
+    Returns (topk_weights [T,k] fp64, topk_indices [T,k] int64,
+    shared_gammas [T,S] fp64, scores [T,E] fp64).  The weights come from the
+    unbiased logits: softmax(log sigma([z_sel || z_shared])) * rs * gs.
+    """
+    z = _f64(z)
+    zr, zs = z[:, :n_routed], z[:, n_routed:]
+    s = selection_scores(zr, bias)
+    idx = topk_select(s, top_k)
+    z_sel = np.take_along_axis(zr, idx, axis=1)
+    ell = log_sigmoid(np.concatenate([z_sel, zs], axis=1))
+    gam = softmax(ell, axis=1) * (float(route_scale) * float(global_scale))
+    return gam[:, :top_k], idx.astype(np.int64), gam[:, top_k:], s
+
+
+def topk_margin(scores, k: int) -> np.ndarray:
+    """s_(k) - s_(k+1) per token (inf when k == E): how far the k-th pick is from
+    the first one left out; used to report near-ties."""
+    s = -np.sort(-_f64(scores), axis=1)
+    if k >= s.shape[1]:
+        return np.full(s.shape[0], np.inf)
+    return s[:, k - 1] - s[:, k]
+
+
+# --------------------------------------------------------------------------
+# Token permutation (dispatch to GroupedExperts)
+# --------------------------------------------------------------------------
+
+def permutation(topk_indices, n_routed: int, token_mask=None):
+    """Expert-sorted order of the routed slots.
+
+    slot = t * k + i.  counts[e] = number of slots routed to e; offsets =
+    exclusive prefix sum (length E+1); sorted_slots lists the slots of expert 0,
+    then expert 1, ..., each in ascending slot order.  Tokens whose mask entry
+    is True (padding) are left out (InklingMoE.forward: padded tokens are
+    excluded from routed-expert dispatch).
+    Returns (counts int64 [E], offsets int64 [E+1], sorted_slots int64 [n]).
+    """
+    idx = np.asarray(topk_indices, dtype=np.int64)
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    slots = np.arange(T * k, dtype=np.int64)
+    if token_mask is not None:
+        keep = ~np.repeat(np.asarray(token_mask, dtype=bool), k)
+        flat, slots = flat[keep], slots[keep]
+    counts = np.bincount(flat, minlength=n_routed).astype(np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    return counts, offsets, slots[order]
+
+
+# --------------------------------------------------------------------------
+# Experts (inkling_swiglu, InklingSharedExperts)
+# --------------------------------------------------------------------------
+
+def silu(v) -> np.ndarray:
+    v = _f64(v)
+    return v * sigmoid(v)
+
+
+def swiglu_interleaved(h, routing_weights=None) -> np.ndarray:
+    """inkling_swiglu: last axis interleaves [g0, u0, g1, u1, ...] (::2 gate,
+    1::2 up); result silu(g) * u, scaled by routing_weights broadcast to
+    [..., I]."""
+    h = _f64(h)
+    a = silu(h[..., 0::2]) * h[..., 1::2]
+    if routing_weights is not None:
+        a = a * _f64(routing_weights)
+    return a
+
+
+def expert_ffn(rows, w_gu, w_d, routing_weights=None) -> np.ndarray:
+    """down_proj(inkling_swiglu(gate_up_proj(rows), w)) with nn.Linear layouts
+    gate_up [2I, H] and down [H, I]."""
+    h = _f64(rows) @ _f64(w_gu).T
+    return swiglu_interleaved(h, routing_weights) @ _f64(w_d).T
+
+
+def shared_experts(x, wsh_gu, wsh_d, gammas) -> np.ndarray:
+    """InklingSharedExperts.forward: sum over s of gamma[:, s] * expert_s(x);
+    the gammas weight each expert's output before the summation."""
+    x = _f64(x)
+    g = _f64(gammas)
+    out = np.zeros((x.shape[0], _f64(wsh_d[0]).shape[0] if len(wsh_d) else x.shape[1]), dtype=F64)
+    for s in range(len(wsh_gu)):
+        out += g[:, s:s + 1] * expert_ffn(x, wsh_gu[s], wsh_d[s])
+    return out
+
+
+# --------------------------------------------------------------------------
+# InklingMoE.forward
+# --------------------------------------------------------------------------
+
+def moe_forward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int,
+                route_scale: float, global_scale: float, padding_mask=None,
+                tokens=None, routing=None):
+    """Output of the layer in fp64.
+
+    x [T, H]; w_gu[e] [2I, H]; w_d[e] [H, I] for e < E (any sequence indexable
+    per expert that yields arrays: weights are widened one expert at a time);
+    wsh_* likewise for the S shared experts.  `tokens` (optional) restricts the
+    output to those token rows (routing still covers every token, so counts and
+    the permutation stay those of the full batch).  `routing` may pass a route()
+    result computed earlier for the same inputs.
+
+    Returns (out [len(tokens) or T, H] fp64, routing dict).
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    E = _f64(bias).shape[0]
+    if routing is None:
+        z = gate_logits(x, gate_bank)
+        tw, ti, sg, s = route(z, bias, E, top_k, route_scale, global_scale)
+        counts, offsets, sorted_slots = permutation(ti, E, padding_mask)
+        routing = dict(logits=z, topk_weights=tw, topk_indices=ti, shared_gammas=sg,
+                       scores=s, counts=counts, offsets=offsets, sorted_slots=sorted_slots)
+    tw, ti, sg = routing["topk_weights"], routing["topk_indices"], routing["shared_gammas"]
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    pad = np.zeros(T, dtype=bool) if padding_mask is None else np.asarray(padding_mask, dtype=bool)
+    xr = x[rows]
+    H = x.shape[1]
+    out = np.zeros((len(rows), H), dtype=F64)
+    # routed experts, one expert at a time over the (token, choice) pairs it received
+    local_t, local_i = np.nonzero(ti[rows] >= 0)
+    sel_e = ti[rows][local_t, local_i]
+    live = ~pad[rows][local_t]
+    local_t, local_i, sel_e = local_t[live], local_i[live], sel_e[live]
+    for e in np.unique(sel_e):
+        m = sel_e == e
+        lt, li = local_t[m], local_i[m]
+        y = expert_ffn(xr[lt], w_gu[e], w_d[e], tw[rows][lt, li][:, None])
+        np.add.at(out, lt, y)
+    if len(wsh_gu):
+        out += shared_experts(xr, wsh_gu, wsh_d, sg[rows])
+    return out, routing
