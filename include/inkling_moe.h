@@ -1,0 +1,169 @@
+/*
+ * inkling_moe.h -- C ABI of the MI355X (gfx950) Inkling MoE feed-forward.
+ *
+ * The operation is the MoE feed-forward of the Inkling layers page
+ * (nemo_automodel.components.models.inkling.layers):
+ *
+ *   InklingGate        logits z = x . bank^T over a gate bank of n_routed routed
+ *                      rows followed by n_shared shared rows, fp32 operands;
+ *                      experts selected by top_k of sigmoid(z) + correction
+ *                      bias (InklingCorrectionBias); weights = softmax of
+ *                      log-sigmoid over [selected routed logits || shared
+ *                      logits] times route_scale * global_scale.
+ *   inkling_swiglu     SwiGLU on the interleaved [g0, u0, g1, u1, ...] gate_up
+ *                      output, the activated output scaled by the routing weight.
+ *   InklingSharedExperts  always-on experts weighted by the shared gammas.
+ *   InklingMoE.forward routed + shared outputs summed; output shaped like the
+ *                      input; padded tokens excluded from routed dispatch.
+ *
+ * Readings where the page is silent: equal selection scores go to the lower
+ * expert index and topk_* are ordered by descending score; route_scale *
+ * global_scale also scales the shared gammas; silu(gate) * up without clamp;
+ * padded tokens still pass through the shared experts.
+ *
+ * Conventions
+ *   - Every tensor pointer is a DEVICE pointer to a contiguous row-major buffer
+ *     owned by the caller.  The library keeps no pointer after a call returns.
+ *   - dtype applies to x and the expert weights (INKLING_F32 or INKLING_BF16);
+ *     out_dtype to the output (the input's dtype is the layer's own choice;
+ *     INKLING_F32 returns the fp32 sum before its final rounding, and a bf16
+ *     output is exactly that sum rounded to nearest-even).  The gate bank and
+ *     correction bias are always fp32; routing outputs are int32 / fp32.
+ *   - Weight layouts are nn.Linear [out, in]:
+ *       routed_gate_up [n_routed][2*I][hidden]  row 2j = gate_j, 2j+1 = up_j
+ *       routed_down    [n_routed][hidden][I]
+ *       shared_gate_up [n_shared][2*I][hidden]  (NULL iff n_shared == 0)
+ *       shared_down    [n_shared][hidden][I]
+ *   - The caller flattens leading dimensions of the hidden states to T rows.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and is asynchronous.  The library never allocates device memory, never
+ *     frees, never synchronises.  Scratch lives in the caller's workspace.
+ *     Calls that share a workspace must be ordered on one stream.
+ *   - Arguments are checked on the host before anything is launched; an error
+ *     return means nothing was enqueued (except INKLING_ERR_HIP, which reports
+ *     a failed launch).
+ *
+ * Limits (INKLING_ERR_UNSUPPORTED otherwise): hidden % 128 == 0,
+ * intermediate % 64 == 0, 1 <= top_k <= min(n_routed, 32), n_routed <= 512,
+ * n_shared <= 16.
+ */
+#ifndef INKLING_MOE_H
+#define INKLING_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define INKLING_OK 0
+#define INKLING_ERR_INVALID_ARGUMENT (-1) /* null required pointer, negative size, top_k > n_routed, ... */
+#define INKLING_ERR_UNSUPPORTED (-2)      /* dtype or size outside the limits above */
+#define INKLING_ERR_WORKSPACE (-3)        /* workspace NULL or smaller than inkling_moe_workspace_size() */
+#define INKLING_ERR_HIP (-4)              /* a HIP launch failed; see inkling_moe_last_hip_error() */
+
+typedef enum { INKLING_F32 = 0, INKLING_BF16 = 1 } inkling_dtype_t;
+
+/* Sizes of one call.  T may be 0 (a successful no-op). */
+typedef struct {
+    int64_t T;            /* tokens (rows of x)                                 */
+    int32_t hidden;       /* H: model width                                     */
+    int32_t n_routed;     /* E: routed experts (InklingGate.num_experts)        */
+    int32_t top_k;        /* k: experts per token (num_experts_per_tok)         */
+    int32_t n_shared;     /* S: always-on shared experts (may be 0)             */
+    int32_t intermediate; /* I: expert intermediate size (moe_intermediate_size)*/
+    int32_t dtype;        /* inkling_dtype_t of x and the expert weights         */
+    int32_t out_dtype;    /* inkling_dtype_t of out (the layer output): usually  */
+                          /* dtype; INKLING_F32 keeps the fp32 sum unrounded     */
+} inkling_moe_dims_t;
+
+/* InklingGate parameters. */
+typedef struct {
+    const float* gate_bank;       /* [n_routed + n_shared][hidden] fp32: routed rows, then shared rows */
+    const float* correction_bias; /* [n_routed] fp32 e_score_correction_bias                           */
+    float route_scale;            /* InklingGate.route_scale                                           */
+    float global_scale;           /* InklingGate.global_scale                                          */
+} inkling_gate_t;
+
+/* Expert weights (layouts above). */
+typedef struct {
+    const void* routed_gate_up;
+    const void* routed_down;
+    const void* shared_gate_up;
+    const void* shared_down;
+} inkling_experts_t;
+
+/*
+ * Routing outputs (InklingGate.forward returns topk_weights, topk_indices and
+ * shared_gammas).  In inkling_moe_route the first three are required; in
+ * inkling_moe_forward the whole struct pointer may be NULL and any member may be
+ * NULL (then it is kept in the workspace only).
+ *   topk_indices  [T][top_k] int32: selected experts, descending biased score,
+ *                 equal scores -> lower index first.
+ *   topk_weights  [T][top_k] fp32: gammas of the selected routed experts.
+ *   shared_gammas [T][n_shared] fp32.
+ *   expert_counts [n_routed] int32: routed (token, choice) pairs per expert,
+ *                 padded tokens excluded.
+ *   expert_offsets[n_routed + 1] int32: exclusive prefix sum of the counts.
+ *   sorted_slots  [T * top_k] int32: slots t*top_k + i grouped by expert
+ *                 (expert 0 first), ascending within an expert; only the first
+ *                 expert_offsets[n_routed] entries are written.
+ */
+typedef struct {
+    int32_t* topk_indices;
+    float* topk_weights;
+    float* shared_gammas;
+    int32_t* expert_counts;
+    int32_t* expert_offsets;
+    int32_t* sorted_slots;
+} inkling_route_out_t;
+
+/* Bytes of device workspace that inkling_moe_route / inkling_moe_forward need
+ * for these sizes (256-byte aligned base expected).  Returns INKLING_OK and
+ * writes *bytes, or an error code for invalid / unsupported sizes. */
+int inkling_moe_workspace_size(const inkling_moe_dims_t* dims, size_t* bytes);
+
+/* InklingGate.forward plus the expert-sorted permutation.
+ *   x             [T][hidden] in dims->dtype.
+ *   padding_mask  [T] uint8, nonzero = padded token (excluded from the counts,
+ *                 offsets and sorted slots; its topk_* entries are still
+ *                 written), or NULL.                                          */
+int inkling_moe_route(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                      const uint8_t* padding_mask, inkling_route_out_t* route_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* InklingMoE.forward: out[T][hidden] (dims->out_dtype) = sum over the selected
+ * routed experts and all shared experts of gamma * expert(x).  out must not
+ * alias x.  padding_mask as above (padded tokens get the shared experts only).
+ * route_out may be NULL. */
+int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                        const inkling_experts_t* experts, const uint8_t* padding_mask, void* out,
+                        inkling_route_out_t* route_out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Stage timing (instrumentation for benchmarks).  When `events` is non-NULL,
+ * each later inkling_moe_forward on the calling thread records, on its stream,
+ * events[0] before the first launch and events[i] after stage i:
+ *   1 router logits, 2 router selection, 3 permutation (masks, scan, scatter),
+ *   4 gate_up grouped GEMM + SwiGLU (routed and shared),
+ *   5 down grouped GEMM (routed), 6 shared down GEMM + combine.
+ * events[] holds INKLING_STAGE_EVENTS hipEvent_t handles created by the caller;
+ * the array must stay valid until the hook is cleared with NULL.  Adds no
+ * synchronisation.  Returns INKLING_ERR_INVALID_ARGUMENT if n_events is too
+ * small. */
+#define INKLING_STAGE_EVENTS 7
+int inkling_moe_set_stage_events(void* const* events, int n_events);
+
+/* Static text for a return code. */
+const char* inkling_moe_strerror(int code);
+
+/* The hipError_t of the last INKLING_ERR_HIP on the calling thread (0 if none). */
+int inkling_moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INKLING_MOE_H */

@@ -1,0 +1,263 @@
+// C ABI of the gfx950 Inkling MoE feed-forward: argument checks, workspace
+// layout and the launch sequence (router -> permutation -> grouped GEMMs).
+#include <string.h>
+
+#include "../../include/inkling_moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace inkling;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+thread_local void* const* g_stage_events = nullptr;
+
+inline hipError_t mark(int i, hipStream_t s) {
+    if (g_stage_events == nullptr) return hipSuccess;
+    return hipEventRecord((hipEvent_t)g_stage_events[i], s);
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    int ksplit, W, cfg, bm, max_tiles;
+    size_t zpart, topk_idx, topk_w, shared_g, masks, prefix, counts, offsets, tiles, num_tiles;
+    size_t sorted_slots, row_token, row_gamma, pos, act_r, act_sh, y, total;
+};
+
+int check_dims(const inkling_moe_dims_t* d) {
+    if (d == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    if (d->T < 0 || d->hidden <= 0 || d->n_routed <= 0 || d->top_k <= 0 || d->n_shared < 0 ||
+        d->intermediate <= 0)
+        return INKLING_ERR_INVALID_ARGUMENT;
+    if (d->top_k > d->n_routed) return INKLING_ERR_INVALID_ARGUMENT;
+    if (d->dtype != INKLING_F32 && d->dtype != INKLING_BF16) return INKLING_ERR_UNSUPPORTED;
+    if (d->out_dtype != INKLING_F32 && d->out_dtype != INKLING_BF16) return INKLING_ERR_UNSUPPORTED;
+    if (d->hidden % 128 != 0 || d->intermediate % 64 != 0) return INKLING_ERR_UNSUPPORTED;
+    if (d->n_routed > 512 || d->n_routed + d->n_shared > 512 || d->top_k > 32 || d->n_shared > 16)
+        return INKLING_ERR_UNSUPPORTED;
+    // int32 row / slot indices
+    if (d->T * (int64_t)d->top_k > INT32_MAX) return INKLING_ERR_UNSUPPORTED;
+    return INKLING_OK;
+}
+
+Layout make_layout(const inkling_moe_dims_t* d) {
+    Layout L = {};
+    const int64_t T = d->T;
+    const int E = d->n_routed, S = d->n_shared, k = d->top_k, H = d->hidden, I = d->intermediate;
+    const size_t es = d->dtype == INKLING_BF16 ? 2 : 4;
+    const int NE = E + S;
+    L.ksplit = router_ksplit((int)T, H, NE);
+    L.W = (int)((T + 63) / 64);
+    L.cfg = gemm_cfg_for(d->dtype, (int)T, H, E, k, I);
+    L.bm = gemm_cfg_bm(L.cfg);
+    L.max_tiles = (int)((T * k + L.bm - 1) / L.bm) + E;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.zpart = take((size_t)L.ksplit * T * NE * sizeof(double));
+    L.topk_idx = take((size_t)T * k * 4);
+    L.topk_w = take((size_t)T * k * 4);
+    L.shared_g = take((size_t)T * S * 4);
+    L.masks = take((size_t)E * L.W * 8);
+    L.prefix = take((size_t)E * L.W * 4);
+    L.counts = take((size_t)E * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.tiles = take((size_t)L.max_tiles * sizeof(RoutedTile));
+    L.num_tiles = take(4);
+    L.sorted_slots = take((size_t)T * k * 4);
+    L.row_token = take((size_t)T * k * 4);
+    L.row_gamma = take((size_t)T * k * 4);
+    L.pos = take((size_t)T * k * 4);
+    L.act_r = take((size_t)T * k * I * es);
+    L.act_sh = take((size_t)T * S * I * es);
+    L.y = take((size_t)T * k * H * sizeof(float));
+    L.total = o;
+    return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+    return reinterpret_cast<P*>(reinterpret_cast<uint8_t*>(ws) + off);
+}
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return INKLING_ERR_HIP;
+}
+
+#define HIP_TRY(expr)                          \
+    do {                                       \
+        hipError_t _e = (expr);                \
+        if (_e != hipSuccess) return hip_fail(_e); \
+    } while (0)
+
+int check_gate(const inkling_gate_t* g) {
+    if (g == nullptr || g->gate_bank == nullptr || g->correction_bias == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    return INKLING_OK;
+}
+
+// Router and permutation shared by both entry points.  Writes the routing
+// outputs into `r` (pointers already resolved to caller or workspace buffers).
+struct RouteBufs {
+    int32_t* topk_idx;
+    float* topk_w;
+    float* shared_g;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_slots;
+    int32_t* row_token;
+    float* row_gamma;
+    int32_t* pos;
+    RoutedTile* tiles;
+    int32_t* num_tiles;
+};
+
+int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const inkling_gate_t* g,
+              const uint8_t* pad, const RouteBufs& rb, bool permute, void* ws, hipStream_t s) {
+    const int T = (int)d->T, E = d->n_routed, S = d->n_shared, k = d->top_k, H = d->hidden;
+    double* zpart = at<double>(ws, L.zpart);
+    HIP_TRY(launch_router_logits(d->dtype, x, g->gate_bank, zpart, T, H, E + S, L.ksplit, s));
+    HIP_TRY(mark(1, s));
+    HIP_TRY(launch_router_select(zpart, L.ksplit, g->correction_bias, T, E, S, k, g->route_scale, g->global_scale,
+                                 rb.topk_idx, rb.topk_w, rb.shared_g, s));
+    HIP_TRY(mark(2, s));
+    if (!permute) return INKLING_OK;
+    uint64_t* masks = at<uint64_t>(ws, L.masks);
+    int32_t* prefix = at<int32_t>(ws, L.prefix);
+    HIP_TRY(launch_build_masks(rb.topk_idx, pad, T, E, k, masks, L.W, s));
+    HIP_TRY(launch_scan(masks, L.W, E, prefix, rb.counts, rb.offsets, rb.tiles ? L.bm : 0, rb.tiles, rb.num_tiles,
+                        s));
+    HIP_TRY(launch_scatter(rb.topk_idx, rb.topk_w, pad, masks, prefix, rb.offsets, T, E, k, L.W, rb.sorted_slots,
+                           rb.row_token, rb.row_gamma, rb.pos, s));
+    HIP_TRY(mark(3, s));
+    return INKLING_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int inkling_moe_workspace_size(const inkling_moe_dims_t* dims, size_t* bytes) {
+    int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (bytes == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    *bytes = make_layout(dims).total;
+    return INKLING_OK;
+}
+
+int inkling_moe_route(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                      const uint8_t* padding_mask, inkling_route_out_t* r, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (dims->T == 0) return INKLING_OK;
+    if (x == nullptr || (rc = check_gate(gate)) != INKLING_OK) return INKLING_ERR_INVALID_ARGUMENT;
+    if (r == nullptr || r->topk_indices == nullptr || r->topk_weights == nullptr ||
+        (dims->n_shared > 0 && r->shared_gammas == nullptr))
+        return INKLING_ERR_INVALID_ARGUMENT;
+    const Layout L = make_layout(dims);
+    if (workspace == nullptr || workspace_bytes < L.total) return INKLING_ERR_WORKSPACE;
+    RouteBufs rb = {};
+    rb.topk_idx = r->topk_indices;
+    rb.topk_w = r->topk_weights;
+    rb.shared_g = r->shared_gammas ? r->shared_gammas : at<float>(workspace, L.shared_g);
+    const bool permute = r->expert_counts || r->expert_offsets || r->sorted_slots;
+    rb.counts = r->expert_counts;
+    rb.offsets = r->expert_offsets ? r->expert_offsets : at<int32_t>(workspace, L.offsets);
+    rb.sorted_slots = r->sorted_slots;
+    return run_route(dims, L, x, gate, padding_mask, rb, permute, workspace, (hipStream_t)stream);
+}
+
+int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                        const inkling_experts_t* w, const uint8_t* padding_mask, void* out,
+                        inkling_route_out_t* r, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (dims->T == 0) return INKLING_OK;
+    if (x == nullptr || out == nullptr || check_gate(gate) != INKLING_OK || w == nullptr)
+        return INKLING_ERR_INVALID_ARGUMENT;
+    if (w->routed_gate_up == nullptr || w->routed_down == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    if (dims->n_shared > 0 && (w->shared_gate_up == nullptr || w->shared_down == nullptr))
+        return INKLING_ERR_INVALID_ARGUMENT;
+    if (out == x) return INKLING_ERR_INVALID_ARGUMENT;
+    const Layout L = make_layout(dims);
+    if (workspace == nullptr || workspace_bytes < L.total) return INKLING_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    RouteBufs rb = {};
+    rb.topk_idx = (r && r->topk_indices) ? r->topk_indices : at<int32_t>(workspace, L.topk_idx);
+    rb.topk_w = (r && r->topk_weights) ? r->topk_weights : at<float>(workspace, L.topk_w);
+    rb.shared_g = (r && r->shared_gammas) ? r->shared_gammas : at<float>(workspace, L.shared_g);
+    rb.counts = (r && r->expert_counts) ? r->expert_counts : at<int32_t>(workspace, L.counts);
+    rb.offsets = (r && r->expert_offsets) ? r->expert_offsets : at<int32_t>(workspace, L.offsets);
+    rb.sorted_slots = (r && r->sorted_slots) ? r->sorted_slots : at<int32_t>(workspace, L.sorted_slots);
+    rb.row_token = at<int32_t>(workspace, L.row_token);
+    rb.row_gamma = at<float>(workspace, L.row_gamma);
+    rb.pos = at<int32_t>(workspace, L.pos);
+    rb.tiles = at<RoutedTile>(workspace, L.tiles);
+    rb.num_tiles = at<int32_t>(workspace, L.num_tiles);
+    HIP_TRY(mark(0, s));
+    rc = run_route(dims, L, x, gate, padding_mask, rb, true, workspace, s);
+    if (rc != INKLING_OK) return rc;
+
+    MoeGemmParams p = {};
+    p.dtype = dims->dtype;
+    p.out_dtype = dims->out_dtype;
+    p.cfg = L.cfg;
+    p.T = (int)dims->T;
+    p.H = dims->hidden;
+    p.E = dims->n_routed;
+    p.S = dims->n_shared;
+    p.I = dims->intermediate;
+    p.k = dims->top_k;
+    p.x = x;
+    p.w_gu = w->routed_gate_up;
+    p.w_d = w->routed_down;
+    p.wsh_gu = w->shared_gate_up;
+    p.wsh_d = w->shared_down;
+    p.tiles = rb.tiles;
+    p.num_tiles = rb.num_tiles;
+    p.offsets = rb.offsets;
+    p.row_token = rb.row_token;
+    p.row_gamma = rb.row_gamma;
+    p.shared_g = rb.shared_g;
+    p.pos = rb.pos;
+    p.act_r = at<void>(workspace, L.act_r);
+    p.act_sh = at<void>(workspace, L.act_sh);
+    p.y = at<void>(workspace, L.y);
+    p.out = out;
+    p.max_routed_tiles = L.max_tiles;
+    HIP_TRY(launch_gate_up(p, s));
+    HIP_TRY(mark(4, s));
+    HIP_TRY(launch_down_routed(p, s));
+    HIP_TRY(mark(5, s));
+    HIP_TRY(launch_down_shared_combine(p, s));
+    HIP_TRY(mark(6, s));
+    return INKLING_OK;
+}
+
+const char* inkling_moe_strerror(int code) {
+    switch (code) {
+        case INKLING_OK: return "success";
+        case INKLING_ERR_INVALID_ARGUMENT: return "invalid argument (null pointer, negative size or top_k > n_routed)";
+        case INKLING_ERR_UNSUPPORTED: return "unsupported dtype or size";
+        case INKLING_ERR_WORKSPACE: return "workspace missing or too small";
+        case INKLING_ERR_HIP: return "HIP launch failed (see inkling_moe_last_hip_error)";
+        default: return "unknown error code";
+    }
+}
+
+int inkling_moe_last_hip_error(void) { return g_last_hip_error; }
+
+int inkling_moe_set_stage_events(void* const* events, int n_events) {
+    if (events != nullptr && n_events < INKLING_STAGE_EVENTS) return INKLING_ERR_INVALID_ARGUMENT;
+    g_stage_events = events;
+    return INKLING_OK;
+}
+
+}  // extern "C"

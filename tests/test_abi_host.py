@@ -1,0 +1,133 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes its workspace, and rejects bad arguments on the host
+before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_feed_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "inkling_moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from mixture_experts_feed_amd import build
+        build.build(verbose=False)
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(inkling_moe_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _dims(**kw):
+    d = dict(T=64, hidden=128, n_routed=8, top_k=2, n_shared=1, intermediate=64, dtype=B.INKLING_BF16,
+             out_dtype=B.INKLING_BF16)
+    d.update(kw)
+    return B.Dims(d["T"], d["hidden"], d["n_routed"], d["top_k"], d["n_shared"], d["intermediate"], d["dtype"],
+                  d["out_dtype"])
+
+
+def _ws(lib, **kw):
+    n = ctypes.c_size_t(0)
+    rc = lib.inkling_moe_workspace_size(ctypes.byref(_dims(**kw)), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    rc0, n0 = _ws(lib, T=0)
+    rc1, n1 = _ws(lib, T=64)
+    rc2, n2 = _ws(lib, T=4096)
+    assert rc0 == rc1 == rc2 == B.INKLING_OK
+    assert 0 <= n0 < n1 < n2
+    # the per-slot down-projection rows dominate: T*k*H*elem bytes
+    assert n2 >= 4096 * 2 * 128 * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(top_k=9), B.INKLING_ERR_INVALID_ARGUMENT),      # top_k > n_routed
+    (dict(top_k=0), B.INKLING_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), B.INKLING_ERR_INVALID_ARGUMENT),
+    (dict(n_shared=-1), B.INKLING_ERR_INVALID_ARGUMENT),
+    (dict(hidden=0), B.INKLING_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), B.INKLING_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), B.INKLING_ERR_UNSUPPORTED),
+    (dict(hidden=96), B.INKLING_ERR_UNSUPPORTED),          # hidden % 128
+    (dict(intermediate=48), B.INKLING_ERR_UNSUPPORTED),    # intermediate % 64
+    (dict(n_routed=600, top_k=2), B.INKLING_ERR_UNSUPPORTED),
+    (dict(n_routed=64, top_k=33), B.INKLING_ERR_UNSUPPORTED),
+    (dict(n_shared=17), B.INKLING_ERR_UNSUPPORTED),
+])
+def test_invalid_dims_rejected(lib, kw, code):
+    rc, _ = _ws(lib, **kw)
+    assert rc == code
+    d = _dims(**kw)
+    fake = ctypes.c_void_p(0x1000)
+    gate = B.Gate(0x1000, 0x1000, 1.0, 1.0)
+    ex = B.Experts(0x1000, 0x1000, 0x1000, 0x1000)
+    rc = lib.inkling_moe_forward(ctypes.byref(d), fake, ctypes.byref(gate), ctypes.byref(ex), None,
+                                 ctypes.c_void_p(0x2000), None, fake, 1 << 40, None)
+    assert rc == code
+
+
+def test_null_pointers_and_small_workspace_rejected(lib):
+    d = _dims()
+    gate = B.Gate(0x1000, 0x1000, 1.0, 1.0)
+    ex = B.Experts(0x1000, 0x1000, 0x1000, 0x1000)
+    ws = ctypes.c_void_p(0x3000)
+    x = ctypes.c_void_p(0x4000)
+    out = ctypes.c_void_p(0x5000)
+    fwd = lib.inkling_moe_forward
+    assert fwd(ctypes.byref(d), None, ctypes.byref(gate), ctypes.byref(ex), None, out, None, ws, 1 << 40,
+               None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert fwd(ctypes.byref(d), x, None, ctypes.byref(ex), None, out, None, ws, 1 << 40,
+               None) == B.INKLING_ERR_INVALID_ARGUMENT
+    bad_gate = B.Gate(None, 0x1000, 1.0, 1.0)
+    assert fwd(ctypes.byref(d), x, ctypes.byref(bad_gate), ctypes.byref(ex), None, out, None, ws, 1 << 40,
+               None) == B.INKLING_ERR_INVALID_ARGUMENT
+    no_shared = B.Experts(0x1000, 0x1000, None, None)
+    assert fwd(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(no_shared), None, out, None, ws, 1 << 40,
+               None) == B.INKLING_ERR_INVALID_ARGUMENT
+    # out aliasing x
+    assert fwd(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, x, None, ws, 1 << 40,
+               None) == B.INKLING_ERR_INVALID_ARGUMENT
+    # workspace too small / missing
+    assert fwd(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, out, None, ws, 16,
+               None) == B.INKLING_ERR_WORKSPACE
+    assert fwd(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, out, None, None, 1 << 40,
+               None) == B.INKLING_ERR_WORKSPACE
+    # route: required outputs
+    ro = B.RouteOut(None, 0x1000, 0x1000, None, None, None)
+    assert lib.inkling_moe_route(ctypes.byref(d), x, ctypes.byref(gate), None, ctypes.byref(ro), ws, 1 << 40,
+                                 None) == B.INKLING_ERR_INVALID_ARGUMENT
+    ro = B.RouteOut(0x1000, 0x1000, 0x1000, None, None, None)
+    assert lib.inkling_moe_route(ctypes.byref(d), x, ctypes.byref(gate), None, ctypes.byref(ro), ws, 8,
+                                 None) == B.INKLING_ERR_WORKSPACE
+
+
+def test_zero_tokens_is_a_noop(lib):
+    d = _dims(T=0)
+    gate = B.Gate(None, None, 1.0, 1.0)
+    assert lib.inkling_moe_forward(ctypes.byref(d), None, ctypes.byref(gate), None, None, None, None, None, 0,
+                                   None) == B.INKLING_OK
+    assert lib.inkling_moe_route(ctypes.byref(d), None, None, None, None, None, 0, None) == B.INKLING_OK
+
+
+def test_strerror(lib):
+    for c in (0, -1, -2, -3, -4, -99):
+        assert isinstance(lib.inkling_moe_strerror(c), bytes)
+    assert lib.inkling_moe_last_hip_error() == 0
