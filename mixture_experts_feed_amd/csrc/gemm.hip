@@ -20,6 +20,8 @@
 //                 the reduction), with the routed rows y[pos(t, i)] added in the
 //                 epilogue -> out.  With S = 0 the reduction is empty and the
 //                 kernel is the combine alone.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,8 +31,13 @@ namespace {
 
 enum { kModeGateUp = 0, kModeDown = 1, kModeDownCombine = 2 };
 
-constexpr int kRowBytes = 128;   // bytes of K per row staged per pipeline step
-constexpr int kChunks = kRowBytes / 16;
+// Each pipeline stage holds 64 bytes of K for every A row (weights) and B row
+// (tokens): 32 bf16 or 16 fp32 values, one MFMA k-step.
+constexpr int kRowB = 64;
+constexpr int kCh = kRowB / 16;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void glb_void_t;
 
 struct GemmKArgs {
     const void* A_routed;   // [E][N_r][K_r]
@@ -44,15 +51,15 @@ struct GemmKArgs {
     const float* row_gamma;
     const float* shared_g;
     const int32_t* pos;
-    const void* y;
+    const float* y;
     void* out_routed;
     void* out_shared;
     int T, H, I, S, k;
-    int K_r, N_r;
-    int K_s, N_s;
+    int K_r, N_r, ntn_r;    // routed problem: K, N per expert, N tiles
+    int K_s, N_s, ntn_s;    // shared problem
     int seg_s;              // shared A(n, kk) = A_shared + (kk/seg)*N_s*seg + n*seg + kk%seg
     int shared_blocks, shared_mtiles;
-    int max_routed_tiles;
+    int has_routed;
 };
 
 template <typename TE>
@@ -99,48 +106,118 @@ __device__ __forceinline__ void store4<float>(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-template <typename TE>
-__device__ __forceinline__ void load4f(const TE* p, float* v);
-template <>
-__device__ __forceinline__ void load4f<bf16_t>(const bf16_t* p, float* v) {
-    uint2 q = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(q.x << 16);
-    v[1] = __uint_as_float(q.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(q.y << 16);
-    v[3] = __uint_as_float(q.y & 0xFFFF0000u);
-}
-template <>
-__device__ __forceinline__ void load4f<float>(const float* p, float* v) {
-    float4 q = *reinterpret_cast<const float4*>(p);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
+// expcnt and lgkmcnt left at their maxima so they are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// BN weight rows x BM token rows per workgroup; WN x WM waves (= 4).
-// TE: operand / intermediate type; TO: type of the layer output (combine mode).
-template <typename TE, typename TO, int BN, int BM, int WN, int WM, int MODE>
-__global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmKArgs a) {
-    static_assert(WN * WM == 4, "four waves");
-    constexpr int EPC = 16 / sizeof(TE);          // elements per 16-byte chunk
-    constexpr int BK = kRowBytes / sizeof(TE);    // K elements per step
-    constexpr int WTN = BN / WN, WTM = BM / WM;   // wave tile
-    constexpr int FN = WTN / 16, FM = WTM / 16;
+// s_waitcnt lgkmcnt(0) only (LDS reads); vmcnt and expcnt left at their maxima.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without the implicit wait for all outstanding memory
+// operations, so loads of later pipeline stages stay in flight across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+    __asm__ volatile("s_barrier" ::: "memory");
+}
+
+// Logical tile of block `bid`: blocks are dealt to the 8 XCDs round-robin, so
+// each XCD receives a contiguous range of logical tiles (neighbouring tiles
+// share operands through that XCD's L2).  Returns -1 for blocks beyond the
+// device-side tile count.
+__device__ __forceinline__ int xcd_tile(int bid, int nb_real) {
+    const int per = (nb_real + 7) >> 3;
+    const int loc = bid >> 3;
+    if (loc >= per) return -1;
+    const int L = (bid & 7) * per + loc;
+    return L < nb_real ? L : -1;
+}
+
+// Grouped ordering of an (MT x NT) tile grid: consecutive ids cycle over up to
+// GM row tiles, then advance the column tile.
+template <int GM>
+__device__ __forceinline__ void grouped(int L, int MT, int NT, int& mt, int& nt) {
+    const int gsz = GM * NT;
+    const int g = L / gsz;
+    const int first = g * GM;
+    const int gm = min(GM, MT - first);
+    const int w = L - g * gsz;
+    mt = first + w % gm;
+    nt = w / gm;
+}
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// BN weight rows x BM token rows per workgroup; WN x WM waves (= 4); STAGES
+// LDS pipeline stages filled by direct global->LDS loads.  TE: operand and
+// intermediate type; TO: type of the layer output (combine mode).
+//
+// Each stage is its own __shared__ array and the K loop is unrolled by STAGES,
+// so every LDS read and every LDS-DMA target is a distinct, statically known
+// object: the compiler then needs no wait on in-flight DMA before reading a
+// stage that is already complete, and loads stay STAGES-1 steps ahead.
+template <typename TE, typename TO, int BN, int BM, int WN, int WM, int STAGES, int GM, int MODE>
+__global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs a) {
+    constexpr int NW = WN * WM;                     // waves per workgroup
+    static_assert(NW == 8, "eight waves: two per SIMD");
+    static_assert(STAGES >= 2 && STAGES <= 8, "stages");
+    constexpr int EPC = 16 / sizeof(TE);            // elements per 16-byte chunk
+    constexpr int BK = kRowB / sizeof(TE);          // K elements per stage
+    constexpr int WTN = BN / WN, WTM = BM / WM;     // wave tile
+    constexpr int FN = WTN / 16, FM = WTM / 16;     // 16-row blocks per wave (token blocks interleaved by WM)
     static_assert(FN >= 1 && FM >= 1, "wave tile at least 16x16");
-    constexpr int NA = (BN * kChunks + 255) / 256;
-    constexpr int NB = (BM * kChunks + 255) / 256;
+    static_assert(BN % 64 == 0 && BM % 16 == 0, "tile shape");
+    constexpr int A_BYTES = BN * kRowB, STAGE_BYTES = (BN + BM) * kRowB;
+    constexpr int A_INS = BN / 16, B_INS = BM / 16;     // 1 KB wave loads per stage
+    constexpr int A_PW = A_INS / NW, B_PW = (B_INS + NW - 1) / NW;
+    static_assert(A_INS % NW == 0, "A loads spread evenly over the waves");
+    constexpr int SMALL = 16;
+    // distinct LDS objects per stage (unused ones shrink to SMALL bytes)
+    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGES > 2 ? STAGE_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGES > 3 ? STAGE_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t st4[STAGES > 4 ? STAGE_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t st5[STAGES > 5 ? STAGE_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t st6[STAGES > 6 ? STAGE_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t st7[STAGES > 7 ? STAGE_BYTES : SMALL];
+    auto stage = [&](auto S_) -> uint8_t* {
+        constexpr int sidx = decltype(S_)::value;
+        if constexpr (sidx == 0) return st0;
+        else if constexpr (sidx == 1) return st1;
+        else if constexpr (sidx == 2) return st2;
+        else if constexpr (sidx == 3) return st3;
+        else if constexpr (sidx == 4) return st4;
+        else if constexpr (sidx == 5) return st5;
+        else if constexpr (sidx == 6) return st6;
+        else return st7;
+    };
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BN + BM) * kRowBytes];
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wn0 = (wv % WN) * WTN, wm0 = (wv / WN) * WTM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) wave index
+    const int wn0 = (wv % WN) * WTN, wm = wv / WN;              // token blocks wm, wm+WM, ...
 
     // ---- which tile -------------------------------------------------------
-    int b = blockIdx.x;
-    const bool is_shared = b < a.shared_blocks;
-    int K, N, seg, n0, rows_valid, grow0 = 0, t0 = 0, expert = 0;
+    const int nb_real = a.shared_blocks + (a.has_routed ? (*a.num_tiles) * a.ntn_r : 0);
+    const int L = xcd_tile(blockIdx.x, nb_real);
+    if (L < 0) return;
+    const bool is_shared = L < a.shared_blocks;
+    int K, N, seg, n0, rows_valid, grow0 = 0, t0 = 0;
     const TE* A;
     const TE* Bsrc;
     if (is_shared) {
-        const int mt = b % a.shared_mtiles, nt = b / a.shared_mtiles;
+        int mt, nt;
+        grouped<GM>(L, a.shared_mtiles, a.ntn_s, mt, nt);
         t0 = mt * BM;
         rows_valid = min(BM, a.T - t0);
         n0 = nt * BN;
@@ -150,40 +227,71 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmKArgs a) {
         A = reinterpret_cast<const TE*>(a.A_shared);
         Bsrc = reinterpret_cast<const TE*>(a.B_shared);
     } else {
-        b -= a.shared_blocks;
-        const int ti = b % a.max_routed_tiles, nt = b / a.max_routed_tiles;
-        if (ti >= *a.num_tiles) return;
+        int ti, nt;
+        grouped<GM>(L - a.shared_blocks, *a.num_tiles, a.ntn_r, ti, nt);
         const RoutedTile tl = a.tiles[ti];
-        expert = tl.expert;
-        const int base = a.offsets[expert];
-        rows_valid = min(BM, a.offsets[expert + 1] - base - tl.row_start);
+        const int base = a.offsets[tl.expert];
+        rows_valid = min(BM, a.offsets[tl.expert + 1] - base - tl.row_start);
         grow0 = base + tl.row_start;
         n0 = nt * BN;
         K = a.K_r;
         N = a.N_r;
         seg = a.K_r;
-        A = reinterpret_cast<const TE*>(a.A_routed) + (size_t)expert * a.N_r * a.K_r;
+        A = reinterpret_cast<const TE*>(a.A_routed) + (size_t)tl.expert * a.N_r * a.K_r;
         Bsrc = reinterpret_cast<const TE*>(a.B_routed);
     }
 
-    // ---- per-thread load assignments (16-byte chunks) ----------------------
-    // chunk L = i*256 + tid -> row L / kChunks, chunk L % kChunks
-    const TE* brow[NB];
-    bool bval[NB];
+    // ---- load sources ------------------------------------------------------
+    // A wave load covers 16 rows x 64 B: lane -> row lane/4, LDS chunk lane%4,
+    // which holds the row's logical chunk (lane%4) ^ ((row/2)%4).
+    const int lr = lane >> 2, lp = lane & 3;
+    const TE* a_src[A_PW];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int L = i * 256 + tid;
-        const int r = L / kChunks;
-        bval[i] = (L < BM * kChunks) && (r < rows_valid);
-        brow[i] = Bsrc;
-        if (bval[i]) {
-            size_t row;
-            if (is_shared) row = (size_t)(t0 + r);
-            else if (MODE == kModeGateUp) row = (size_t)a.row_token[grow0 + r];
-            else row = (size_t)(grow0 + r);
-            brow[i] = Bsrc + row * K + (L % kChunks) * EPC;
-        }
+    for (int q = 0; q < A_PW; ++q) {
+        const int r = 16 * (wv + NW * q) + lr;
+        const int c = lp ^ ((r >> 1) & 3);
+        a_src[q] = A + (size_t)min(n0 + r, N - 1) * seg + c * EPC;   // rows past N re-read row N-1
     }
+    const TE* b_src[B_PW];
+#pragma unroll
+    for (int q = 0; q < B_PW; ++q) {
+        const int r = 16 * (wv + NW * q) + lr;
+        const int c = lp ^ ((r >> 1) & 3);
+        const int rr = min(r, rows_valid - 1);   // rows past the end re-read the last valid row
+        size_t row;
+        if (is_shared) row = (size_t)(t0 + rr);
+        else if (MODE == kModeGateUp) row = (size_t)a.row_token[grow0 + rr];
+        else row = (size_t)(grow0 + rr);
+        b_src[q] = Bsrc + row * K + c * EPC;
+    }
+
+    // K offset of A at the next stage to issue: A rows are read in segments of
+    // `seg` columns (the shared down projection concatenates S experts along K)
+    int a_k = 0;
+    size_t a_seg = 0;
+    const size_t a_seg_step = (size_t)N * seg;
+    int next_k = 0;
+    auto issue = [&](auto S_) __attribute__((always_inline)) {
+        uint8_t* __restrict__ sb = stage(S_);
+        const size_t aoff = a_seg + a_k;
+#pragma unroll
+        for (int q = 0; q < A_PW; ++q)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + aoff), (lds_void_t*)(sb + (wv + NW * q) * 1024),
+                                             16, 0, 0);
+#pragma unroll
+        for (int q = 0; q < B_PW; ++q) {
+            const int qi = wv + NW * q;
+            if (qi < B_INS && 16 * qi < rows_valid)
+                __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[q] + next_k),
+                                                 (lds_void_t*)(sb + A_BYTES + qi * 1024), 16, 0, 0);
+        }
+        next_k += BK;
+        a_k += BK;
+        if (a_k == seg) {
+            a_k = 0;
+            a_seg += a_seg_step;
+        }
+    };
 
     f32x4_t acc[FN][FM];
 #pragma unroll
@@ -191,88 +299,106 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmKArgs a) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[NA], rb[NB];
-    auto gload = [&](int k0) {
-        const int s = k0 / seg;
-        const TE* Ab = A + (size_t)s * N * seg + (k0 - s * seg);
+    const int c = lane >> 4;                    // logical chunk this lane feeds to the MFMA
+    const int nk = K / BK;
+    const int rl = lane & 15;
+    // fragment rows: A rows wn0 + 16i + rl, B rows 16*(WM*j + wm) + rl; every
+    // 16-row block keeps the (row/2)%4 swizzle phase of its first row
+    const int a_rd = (wn0 + rl) * kRowB + ((c ^ ((rl >> 1) & 3)) << 4);
+    const int b_rd = A_BYTES + (16 * wm + rl) * kRowB + ((c ^ ((rl >> 1) & 3)) << 4);
+    constexpr int B_STEP = 16 * WM * kRowB;         // bytes between this wave's token blocks
+
+    // NJ: 16-row token blocks computed (blocks past the last valid row skipped).
+    //
+    // Per stage kt (buffer kt % STAGES), with the A fragments and the first H1 B
+    // fragments already read during the previous stage:
+    //   wait LDS reads -> read B blocks H1.. -> MFMAs of blocks 0..H1-1 ->
+    //   wait LDS reads -> wait this wave's DMA for stage kt+1 -> barrier ->
+    //   DMA stage kt+STAGES into buffer kt % STAGES (all waves are done reading it) ->
+    //   read A and B blocks 0..H1-1 of stage kt+1 -> MFMAs of blocks H1..NJ-1.
+    // LDS read latency hides under MFMAs and STAGES-1 stages of loads are in
+    // flight at every barrier.
+    auto kloop = [&](auto NJ_) __attribute__((always_inline)) {
+        constexpr int NJ = decltype(NJ_)::value;
+        constexpr int H1 = (NJ + 1) / 2, H2 = NJ - H1;
+        uint4 fa[FN], fb1[H1], fb2[H2 > 0 ? H2 : 1];
+        auto read_head = [&](const uint8_t* __restrict__ sb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int L = i * 256 + tid;
-            if (L < BN * kChunks) {
-                const int r = L / kChunks, c = L % kChunks;
-                ra[i] = *reinterpret_cast<const uint4*>(Ab + (size_t)(n0 + r) * seg + c * EPC);
-            }
-        }
+            for (int i = 0; i < FN; ++i)   // 16-row blocks keep the (row/2)%4 swizzle phase
+                fa[i] = *reinterpret_cast<const uint4*>(sb + a_rd + i * 16 * kRowB);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            if (bval[i]) rb[i] = *reinterpret_cast<const uint4*>(brow[i] + k0);
-            else rb[i] = make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto sstore = [&](int st) {
-        uint8_t* la = lds[st];
-        uint8_t* lb = lds[st] + BN * kRowBytes;
+            for (int j = 0; j < H1; ++j) fb1[j] = *reinterpret_cast<const uint4*>(sb + b_rd + j * B_STEP);
+        };
+        static_for<0, STAGES>([&](auto S_) {
+            if (decltype(S_)::value < nk) issue(S_);
+        });
+        if (STAGES - 1 < nk) wait_vmcnt<(STAGES - 1) * A_PW>();
+        else wait_vmcnt<0>();
+        barrier_keep_loads();
+        read_head(stage(std::integral_constant<int, 0>{}));
+        for (int kt0 = 0; kt0 < nk; kt0 += STAGES) {
+            static_for<0, STAGES>([&](auto S_) __attribute__((always_inline)) {
+                constexpr int sidx = decltype(S_)::value;
+                const int kt = kt0 + sidx;
+                if (kt < nk) {
+                    const uint8_t* __restrict__ sb = stage(S_);
+                    wait_lgkmcnt0();
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int L = i * 256 + tid;
-            if (L < BN * kChunks) {
-                const int r = L / kChunks, c = L % kChunks;
-                *reinterpret_cast<uint4*>(la + r * kRowBytes + ((c ^ (r & 7)) << 4)) = ra[i];
-            }
-        }
+                    for (int j = 0; j < H2; ++j)
+                        fb2[j] = *reinterpret_cast<const uint4*>(sb + b_rd + (H1 + j) * B_STEP);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int L = i * 256 + tid;
-            if (L < BM * kChunks) {
-                const int r = L / kChunks, c = L % kChunks;
-                *reinterpret_cast<uint4*>(lb + r * kRowBytes + ((c ^ (r & 7)) << 4)) = rb[i];
-            }
+                    for (int j = 0; j < H1; ++j)
+#pragma unroll
+                        for (int i = 0; i < FN; ++i) mma16<TE>(acc[i][j], fa[i], fb1[j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_lgkmcnt0();
+                    uint4 fa_cur[FN];
+#pragma unroll
+                    for (int i = 0; i < FN; ++i) fa_cur[i] = fa[i];
+                    if (kt + 1 < nk) {
+                        if (kt + STAGES - 1 < nk) wait_vmcnt<(STAGES - 2) * A_PW>();
+                        else wait_vmcnt<0>();
+                        barrier_keep_loads();
+                        if (kt + STAGES < nk) issue(S_);
+                        read_head(stage(std::integral_constant<int, (sidx + 1) % STAGES>{}));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < H2; ++j)
+#pragma unroll
+                        for (int i = 0; i < FN; ++i) mma16<TE>(acc[i][H1 + j], fa_cur[i], fb2[j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
         }
     };
 
-    const int nk = K / BK;
-    if (nk > 0) {
-        gload(0);
-        sstore(0);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const uint8_t* la = lds[st];
-        const uint8_t* lb = lds[st] + BN * kRowBytes;
-#pragma unroll
-        for (int s = 0; s < kChunks / 4; ++s) {
-            const int c = 4 * s + (lane >> 4);
-            uint4 af[FN], bfr[FM];
-#pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                const int r = wn0 + 16 * i + (lane & 15);
-                af[i] = *reinterpret_cast<const uint4*>(la + r * kRowBytes + ((c ^ (r & 7)) << 4));
-            }
-#pragma unroll
-            for (int j = 0; j < FM; ++j) {
-                const int r = wm0 + 16 * j + (lane & 15);
-                bfr[j] = *reinterpret_cast<const uint4*>(lb + r * kRowBytes + ((c ^ (r & 7)) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int j = 0; j < FM; ++j) mma16<TE>(acc[i][j], af[i], bfr[j]);
-        }
-        if (kt + 1 < nk) sstore(st ^ 1);
-        __syncthreads();
+    // token blocks / weight-row blocks of this wave that hold valid rows
+    const int nvb_all = (rows_valid + 15) >> 4;
+    const int nvb = min(FM, max(0, (nvb_all - wm + WM - 1) / WM));
+    const int nvi = min(FN, max(0, (N - n0 - wn0 + 15) >> 4));
+    if constexpr (FM == 1) {
+        kloop(std::integral_constant<int, 1>{});
+    } else {
+        // a wave without valid token rows still runs one block, to take part in the
+        // loads and barriers; nothing of it is stored
+        const int nvb_run = max(nvb, 1);
+        static_for<1, FM + 1>([&](auto P_) {
+            if (nvb_run == decltype(P_)::value) kloop(std::integral_constant<int, decltype(P_)::value>{});
+        });
     }
 
     // ---- epilogue ----------------------------------------------------------
-    // acc[i][j][r]: output column n = n0 + wn0 + 16i + 4*(lane/16) + r, row m = wm0 + 16j + lane%16
+    // acc[i][j][r]: output column n = n0 + wn0 + 16i + 4*(lane/16) + r, row m = 16*(WM*j + wm) + lane%16
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-        const int m = wm0 + 16 * j + (lane & 15);
-        if (m >= rows_valid) continue;
+        const int m = 16 * (WM * j + wm) + (lane & 15);
+        if (j >= nvb || m >= rows_valid) continue;
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
             const int n = n0 + wn0 + 16 * i + 4 * (lane >> 4);
+            if (i >= nvi) continue;
             const f32x4_t v = acc[i][j];
             if (MODE == kModeGateUp) {
                 if (is_shared) {
@@ -298,9 +424,8 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmKArgs a) {
                 for (int q = 0; q < a.k; ++q) {
                     const int p = a.pos[(size_t)t * a.k + q];
                     if (p < 0) continue;
-                    float yv[4];
-                    load4f<float>(reinterpret_cast<const float*>(a.y) + (size_t)p * a.H + n, yv);
-                    w[0] += yv[0]; w[1] += yv[1]; w[2] += yv[2]; w[3] += yv[3];
+                    const float4 yv = *reinterpret_cast<const float4*>(a.y + (size_t)p * a.H + n);
+                    w[0] += yv.x; w[1] += yv.y; w[2] += yv.z; w[3] += yv.w;
                 }
                 store4<TO>(reinterpret_cast<TO*>(a.out_shared) + (size_t)t * a.H + n, w);
             }
@@ -309,17 +434,23 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(const GemmKArgs a) {
 }
 
 // ---- tile configurations ---------------------------------------------------
-// cfg 0: 128 weight rows x 128 tokens, waves 2x2 (many rows per expert)
-// cfg 1: 128 weight rows x 16 tokens,  waves 4x1 (few rows per expert: decode)
-constexpr int kBN = 128;
+// cfg 0 (many rows per expert): 256 weight rows x 256 tokens, 8 waves (two per
+//       SIMD) as 4 along the weight rows x 2 along the tokens, each 64 rows x
+//       128 tokens (token blocks interleaved), 4 stages (128 KB LDS).
+// cfg 1 (few rows per expert, decode): 256 weight rows x 16 tokens, 8 waves
+//       along the weight rows, 8 stages.
+constexpr int kBN = 256;
 
 template <typename TE, typename TO, int MODE>
 hipError_t launch_mode(int cfg, const GemmKArgs& a, int blocks, hipStream_t stream) {
     if (blocks <= 0) return hipSuccess;
+    blocks = (blocks + 7) / 8 * 8;
     if (cfg == 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 128, 128, 2, 2, MODE>), dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 256, 4, 2, 4, 2, MODE>), dim3(blocks), dim3(512), 0, stream,
+                           a);
     else
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 128, 16, 4, 1, MODE>), dim3(blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 16, 8, 1, 8, 1, MODE>), dim3(blocks), dim3(512), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
@@ -342,13 +473,12 @@ GemmKArgs base_args(const MoeGemmParams& p) {
     a.row_gamma = p.row_gamma;
     a.shared_g = p.shared_g;
     a.pos = p.pos;
-    a.y = p.y;
+    a.y = reinterpret_cast<const float*>(p.y);
     a.T = p.T;
     a.H = p.H;
     a.I = p.I;
     a.S = p.S;
     a.k = p.k;
-    a.max_routed_tiles = p.max_routed_tiles;
     return a;
 }
 
@@ -360,7 +490,7 @@ int gemm_cfg_for(int dtype, int T, int H, int E, int k, int I) {
     return rows_per_expert <= 48.0 ? 1 : 0;
 }
 
-int gemm_cfg_bm(int cfg) { return cfg == 0 ? 128 : 16; }
+int gemm_cfg_bm(int cfg) { return cfg == 0 ? 256 : 16; }
 
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     GemmKArgs a = base_args(p);
@@ -370,15 +500,18 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     a.out_routed = p.act_r;
     a.K_r = p.H;
     a.N_r = 2 * p.I;
+    a.ntn_r = (a.N_r + kBN - 1) / kBN;
+    a.has_routed = 1;
     a.A_shared = p.wsh_gu;
     a.B_shared = p.x;
     a.out_shared = p.act_sh;
     a.K_s = p.H;
     a.N_s = 2 * p.I * p.S;
+    a.ntn_s = (a.N_s + kBN - 1) / kBN;
     a.seg_s = p.H;
     a.shared_mtiles = (p.T + bm - 1) / bm;
-    a.shared_blocks = p.S > 0 ? a.shared_mtiles * (a.N_s / kBN) : 0;
-    const int blocks = a.shared_blocks + p.max_routed_tiles * (a.N_r / kBN);
+    a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
+    const int blocks = a.shared_blocks + p.max_routed_tiles * a.ntn_r;
     return launch_dispatch<kModeGateUp>(p, a, blocks, stream);
 }
 
@@ -389,9 +522,13 @@ hipError_t launch_down_routed(const MoeGemmParams& p, hipStream_t stream) {
     a.out_routed = p.y;
     a.K_r = p.I;
     a.N_r = p.H;
+    a.ntn_r = (p.H + kBN - 1) / kBN;
+    a.has_routed = 1;
     a.shared_blocks = 0;
     a.shared_mtiles = 1;
-    const int blocks = p.max_routed_tiles * (p.H / kBN);
+    a.ntn_s = 1;
+    a.seg_s = 1;
+    const int blocks = p.max_routed_tiles * a.ntn_r;
     return launch_dispatch<kModeDown>(p, a, blocks, stream);
 }
 
@@ -403,10 +540,11 @@ hipError_t launch_down_shared_combine(const MoeGemmParams& p, hipStream_t stream
     a.out_shared = p.out;
     a.K_s = p.S * p.I;
     a.N_s = p.H;
+    a.ntn_s = (p.H + kBN - 1) / kBN;
     a.seg_s = p.I;
     a.shared_mtiles = (p.T + bm - 1) / bm;
-    a.shared_blocks = a.shared_mtiles * (p.H / kBN);
-    a.max_routed_tiles = 1;
+    a.shared_blocks = a.shared_mtiles * a.ntn_s;
+    a.has_routed = 0;
     return launch_dispatch<kModeDownCombine>(p, a, a.shared_blocks, stream);
 }
 
