@@ -44,7 +44,7 @@
  *     a failed launch).
  *
  * Limits (INKLING_ERR_UNSUPPORTED otherwise): hidden % 64 == 0,
- * intermediate % 32 == 0, 1 <= top_k <= min(n_routed, 32), n_routed <= 512,
+ * intermediate % 64 == 0, 1 <= top_k <= min(n_routed, 32), n_routed <= 512,
  * n_routed + n_shared <= 512, n_shared <= 16, T * top_k < 2^31.
  */
 #ifndef INKLING_MOE_H

@@ -35,7 +35,7 @@ int check_dims(const inkling_moe_dims_t* d) {
     if (d->top_k > d->n_routed) return INKLING_ERR_INVALID_ARGUMENT;
     if (d->dtype != INKLING_F32 && d->dtype != INKLING_BF16) return INKLING_ERR_UNSUPPORTED;
     if (d->out_dtype != INKLING_F32 && d->out_dtype != INKLING_BF16) return INKLING_ERR_UNSUPPORTED;
-    if (d->hidden % 64 != 0 || d->intermediate % 32 != 0) return INKLING_ERR_UNSUPPORTED;
+    if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return INKLING_ERR_UNSUPPORTED;
     if (d->n_routed > 512 || d->n_routed + d->n_shared > 512 || d->top_k > 32 || d->n_shared > 16)
         return INKLING_ERR_UNSUPPORTED;
     // int32 row / slot indices

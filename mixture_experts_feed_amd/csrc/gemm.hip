@@ -31,11 +31,6 @@ namespace {
 
 enum { kModeGateUp = 0, kModeDown = 1, kModeDownCombine = 2 };
 
-// Each pipeline stage holds 64 bytes of K for every A row (weights) and B row
-// (tokens): 32 bf16 or 16 fp32 values, one MFMA k-step.
-constexpr int kRowB = 64;
-constexpr int kCh = kRowB / 16;
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
 
@@ -158,27 +153,32 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// BN weight rows x BM token rows per workgroup; WN x WM waves (= 4); STAGES
-// LDS pipeline stages filled by direct global->LDS loads.  TE: operand and
-// intermediate type; TO: type of the layer output (combine mode).
+// BN weight rows x BM token rows per workgroup; WN x WM waves (8, two per
+// SIMD); STAGES LDS pipeline stages of ROWB bytes of K per row, filled by
+// direct global->LDS loads.  TE: operand and intermediate type; TO: type of
+// the layer output (combine mode).
 //
 // Each stage is its own __shared__ array and the K loop is unrolled by STAGES,
 // so every LDS read and every LDS-DMA target is a distinct, statically known
 // object: the compiler then needs no wait on in-flight DMA before reading a
-// stage that is already complete, and loads stay STAGES-1 steps ahead.
-template <typename TE, typename TO, int BN, int BM, int WN, int WM, int STAGES, int GM, int MODE>
+// stage that is already complete.
+template <typename TE, typename TO, int BN, int BM, int WN, int WM, int STAGES, int ROWB, int GM, int MODE>
 __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs a) {
     constexpr int NW = WN * WM;                     // waves per workgroup
     static_assert(NW == 8, "eight waves: two per SIMD");
     static_assert(STAGES >= 2 && STAGES <= 8, "stages");
+    static_assert(ROWB == 64 || ROWB == 128, "64 or 128 bytes of K per row and stage");
+    constexpr int CH = ROWB / 16;                   // 16-byte chunks per row and stage
+    constexpr int KS = ROWB / 64;                   // MFMA k-steps per stage (64 bytes of K each)
     constexpr int EPC = 16 / sizeof(TE);            // elements per 16-byte chunk
-    constexpr int BK = kRowB / sizeof(TE);          // K elements per stage
+    constexpr int BK = ROWB / sizeof(TE);           // K elements per stage
     constexpr int WTN = BN / WN, WTM = BM / WM;     // wave tile
     constexpr int FN = WTN / 16, FM = WTM / 16;     // 16-row blocks per wave (token blocks interleaved by WM)
     static_assert(FN >= 1 && FM >= 1, "wave tile at least 16x16");
     static_assert(BN % 64 == 0 && BM % 16 == 0, "tile shape");
-    constexpr int A_BYTES = BN * kRowB, STAGE_BYTES = (BN + BM) * kRowB;
-    constexpr int A_INS = BN / 16, B_INS = BM / 16;     // 1 KB wave loads per stage
+    constexpr int RPL = 1024 / ROWB;                // rows per 1 KB wave load
+    constexpr int A_BYTES = BN * ROWB, STAGE_BYTES = (BN + BM) * ROWB;
+    constexpr int A_INS = BN / RPL, B_INS = BM / RPL;   // 1 KB wave loads per stage
     constexpr int A_PW = A_INS / NW, B_PW = (B_INS + NW - 1) / NW;
     static_assert(A_INS % NW == 0, "A loads spread evenly over the waves");
     constexpr int SMALL = 16;
@@ -242,27 +242,27 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     }
 
     // ---- load sources ------------------------------------------------------
-    // A wave load covers 16 rows x 64 B: lane -> row lane/4, LDS chunk lane%4,
-    // which holds the row's logical chunk (lane%4) ^ ((row/2)%4).
-    const int lr = lane >> 2, lp = lane & 3;
+    // LDS rows are ROWB bytes; the 16-byte chunk c of row r sits at chunk
+    // position c ^ sw(r), which makes the fragment reads below conflict-free.
+    // A wave load fills RPL rows: lane -> row lane / CH, chunk position lane % CH.
+    auto sw = [](int r) { return CH == 4 ? ((r >> 1) & 3) : (r & 7); };
+    const int lr = lane / CH, lp = lane % CH;
     const TE* a_src[A_PW];
 #pragma unroll
     for (int q = 0; q < A_PW; ++q) {
-        const int r = 16 * (wv + NW * q) + lr;
-        const int c = lp ^ ((r >> 1) & 3);
-        a_src[q] = A + (size_t)min(n0 + r, N - 1) * seg + c * EPC;   // rows past N re-read row N-1
+        const int r = RPL * (wv + NW * q) + lr;
+        a_src[q] = A + (size_t)min(n0 + r, N - 1) * seg + (lp ^ sw(r)) * EPC;   // rows past N re-read row N-1
     }
     const TE* b_src[B_PW];
 #pragma unroll
     for (int q = 0; q < B_PW; ++q) {
-        const int r = 16 * (wv + NW * q) + lr;
-        const int c = lp ^ ((r >> 1) & 3);
+        const int r = RPL * (wv + NW * q) + lr;
         const int rr = min(r, rows_valid - 1);   // rows past the end re-read the last valid row
         size_t row;
         if (is_shared) row = (size_t)(t0 + rr);
         else if (MODE == kModeGateUp) row = (size_t)a.row_token[grow0 + rr];
         else row = (size_t)(grow0 + rr);
-        b_src[q] = Bsrc + row * K + c * EPC;
+        b_src[q] = Bsrc + row * K + (lp ^ sw(r)) * EPC;
     }
 
     // K offset of A at the next stage to issue: A rows are read in segments of
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 #pragma unroll
         for (int q = 0; q < B_PW; ++q) {
             const int qi = wv + NW * q;
-            if (qi < B_INS && 16 * qi < rows_valid)
+            if (qi < B_INS && RPL * qi < rows_valid)
                 __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[q] + next_k),
                                                  (lds_void_t*)(sb + A_BYTES + qi * 1024), 16, 0, 0);
         }
@@ -299,76 +299,104 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int c = lane >> 4;                    // logical chunk this lane feeds to the MFMA
     const int nk = K / BK;
+    // fragment rows: A rows wn0 + 16i + rl, B rows 16*(WM*j + wm) + rl; 16-row
+    // blocks start at multiples of 8 rows, so sw(row) = sw(rl) throughout.
+    // In k-step s a lane feeds logical chunk 4s + lane/16 to the MFMA.
     const int rl = lane & 15;
-    // fragment rows: A rows wn0 + 16i + rl, B rows 16*(WM*j + wm) + rl; every
-    // 16-row block keeps the (row/2)%4 swizzle phase of its first row
-    const int a_rd = (wn0 + rl) * kRowB + ((c ^ ((rl >> 1) & 3)) << 4);
-    const int b_rd = A_BYTES + (16 * wm + rl) * kRowB + ((c ^ ((rl >> 1) & 3)) << 4);
-    constexpr int B_STEP = 16 * WM * kRowB;         // bytes between this wave's token blocks
+    int a_rd[KS], b_rd[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int cpos = ((4 * s + (lane >> 4)) ^ sw(rl)) << 4;
+        a_rd[s] = (wn0 + rl) * ROWB + cpos;
+        b_rd[s] = A_BYTES + (16 * wm + rl) * ROWB + cpos;
+    }
+    constexpr int A_STEP = 16 * ROWB;               // bytes between a wave's weight-row blocks
+    constexpr int B_STEP = 16 * WM * ROWB;          // bytes between a wave's token blocks
 
     // NJ: 16-row token blocks computed (blocks past the last valid row skipped).
     //
-    // Per stage kt (buffer kt % STAGES), with the A fragments and the first H1 B
-    // fragments already read during the previous stage:
-    //   wait LDS reads -> read B blocks H1.. -> MFMAs of blocks 0..H1-1 ->
-    //   wait LDS reads -> wait this wave's DMA for stage kt+1 -> barrier ->
-    //   DMA stage kt+STAGES into buffer kt % STAGES (all waves are done reading it) ->
-    //   read A and B blocks 0..H1-1 of stage kt+1 -> MFMAs of blocks H1..NJ-1.
-    // LDS read latency hides under MFMAs and STAGES-1 stages of loads are in
-    // flight at every barrier.
+    // Work of a stage = KS k-steps x 2 halves of the token blocks (half-steps).
+    // The LDS fragments of each half-step are read during the previous one:
+    //   wait for the reads issued last half-step -> issue the next half-step's
+    //   reads -> MFMAs of this half-step.
+    // Before the stage's last half-step (all its reads done): wait for this
+    // wave's DMA of stage kt+1, barrier, DMA stage kt+STAGES into the buffer
+    // just freed, then read the first half-step of stage kt+1.
     auto kloop = [&](auto NJ_) __attribute__((always_inline)) {
         constexpr int NJ = decltype(NJ_)::value;
         constexpr int H1 = (NJ + 1) / 2, H2 = NJ - H1;
-        uint4 fa[FN], fb1[H1], fb2[H2 > 0 ? H2 : 1];
-        auto read_head = [&](const uint8_t* __restrict__ sb) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < FN; ++i)   // 16-row blocks keep the (row/2)%4 swizzle phase
-                fa[i] = *reinterpret_cast<const uint4*>(sb + a_rd + i * 16 * kRowB);
-#pragma unroll
-            for (int j = 0; j < H1; ++j) fb1[j] = *reinterpret_cast<const uint4*>(sb + b_rd + j * B_STEP);
-        };
+        constexpr int HS = H2 > 0 ? 2 * KS : KS;    // half-steps per stage
+        static_assert((STAGES % 2) == 0, "even stage count keeps buffer parity static");
+        // fragments double-buffered by the parity of the global k-step (A) and
+        // half-step (B) index; with STAGES even both parities are compile-time
+        uint4 fa[2][FN], fb[2][H1];
         static_for<0, STAGES>([&](auto S_) {
             if (decltype(S_)::value < nk) issue(S_);
         });
         if (STAGES - 1 < nk) wait_vmcnt<(STAGES - 1) * A_PW>();
         else wait_vmcnt<0>();
         barrier_keep_loads();
-        read_head(stage(std::integral_constant<int, 0>{}));
+        {
+            const uint8_t* __restrict__ s0 = stage(std::integral_constant<int, 0>{});
+#pragma unroll
+            for (int i = 0; i < FN; ++i) fa[0][i] = *reinterpret_cast<const uint4*>(s0 + a_rd[0] + i * A_STEP);
+#pragma unroll
+            for (int j = 0; j < H1; ++j) fb[0][j] = *reinterpret_cast<const uint4*>(s0 + b_rd[0] + j * B_STEP);
+        }
         for (int kt0 = 0; kt0 < nk; kt0 += STAGES) {
             static_for<0, STAGES>([&](auto S_) __attribute__((always_inline)) {
                 constexpr int sidx = decltype(S_)::value;
                 const int kt = kt0 + sidx;
                 if (kt < nk) {
                     const uint8_t* __restrict__ sb = stage(S_);
-                    wait_lgkmcnt0();
+                    static_for<0, HS>([&](auto H_) __attribute__((always_inline)) {
+                        constexpr int h = decltype(H_)::value;
+                        constexpr int ks = H2 > 0 ? h >> 1 : h;          // k-step of this half-step
+                        constexpr int half = H2 > 0 ? (h & 1) : 0;       // token half
+                        constexpr int bcur = (sidx * HS + h) & 1;        // B buffer of this half-step
+                        constexpr int acur = (sidx * KS + ks) & 1;       // A buffer of this k-step
+                        wait_lgkmcnt0();
+                        if constexpr (h + 1 < HS) {
+                            // read the next half-step of this stage
+                            constexpr int hn = h + 1;
+                            constexpr int ksn = H2 > 0 ? hn >> 1 : hn;
+                            constexpr int halfn = H2 > 0 ? (hn & 1) : 0;
+                            if constexpr (halfn == 0) {
 #pragma unroll
-                    for (int j = 0; j < H2; ++j)
-                        fb2[j] = *reinterpret_cast<const uint4*>(sb + b_rd + (H1 + j) * B_STEP);
-                    __builtin_amdgcn_sched_barrier(0);
+                                for (int i = 0; i < FN; ++i)
+                                    fa[acur ^ 1][i] = *reinterpret_cast<const uint4*>(sb + a_rd[ksn] + i * A_STEP);
+                            }
+                            constexpr int j0 = halfn ? H1 : 0, jn = halfn ? H2 : H1;
 #pragma unroll
-                    for (int j = 0; j < H1; ++j)
+                            for (int j = 0; j < jn; ++j)
+                                fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(sb + b_rd[ksn] + (j0 + j) * B_STEP);
+                        } else {
+                            if (kt + 1 < nk) {
+                                // all reads of this stage are done: refill it, start the next stage
+                                if (kt + STAGES - 1 < nk) wait_vmcnt<(STAGES - 2) * A_PW>();
+                                else wait_vmcnt<0>();
+                                barrier_keep_loads();
+                                if (kt + STAGES < nk) issue(S_);
+                                constexpr int snext = (sidx + 1) % STAGES;
+                                const uint8_t* __restrict__ sn = stage(std::integral_constant<int, snext>{});
+                                constexpr int an = (snext * KS) & 1;     // A buffer of the next stage's k-step 0
 #pragma unroll
-                        for (int i = 0; i < FN; ++i) mma16<TE>(acc[i][j], fa[i], fb1[j]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    wait_lgkmcnt0();
-                    uint4 fa_cur[FN];
+                                for (int i = 0; i < FN; ++i)
+                                    fa[an][i] = *reinterpret_cast<const uint4*>(sn + a_rd[0] + i * A_STEP);
 #pragma unroll
-                    for (int i = 0; i < FN; ++i) fa_cur[i] = fa[i];
-                    if (kt + 1 < nk) {
-                        if (kt + STAGES - 1 < nk) wait_vmcnt<(STAGES - 2) * A_PW>();
-                        else wait_vmcnt<0>();
-                        barrier_keep_loads();
-                        if (kt + STAGES < nk) issue(S_);
-                        read_head(stage(std::integral_constant<int, (sidx + 1) % STAGES>{}));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                                for (int j = 0; j < H1; ++j)
+                                    fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(sn + b_rd[0] + j * B_STEP);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        constexpr int jbase = half ? H1 : 0, jn = half ? H2 : H1;
 #pragma unroll
-                    for (int j = 0; j < H2; ++j)
+                        for (int j = 0; j < jn; ++j)
 #pragma unroll
-                        for (int i = 0; i < FN; ++i) mma16<TE>(acc[i][H1 + j], fa_cur[i], fb2[j]);
-                    __builtin_amdgcn_sched_barrier(0);
+                            for (int i = 0; i < FN; ++i) mma16<TE>(acc[i][jbase + j], fa[acur][i], fb[bcur][j]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
                 }
             });
         }
@@ -440,17 +468,19 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 // cfg 1 (few rows per expert, decode): 256 weight rows x 16 tokens, 8 waves
 //       along the weight rows, 8 stages.
 constexpr int kBN = 256;
+constexpr int kPrefillStages = 2, kPrefillRowB = 128;
+constexpr int kDecodeStages = 4, kDecodeRowB = 128;
 
 template <typename TE, typename TO, int MODE>
 hipError_t launch_mode(int cfg, const GemmKArgs& a, int blocks, hipStream_t stream) {
     if (blocks <= 0) return hipSuccess;
     blocks = (blocks + 7) / 8 * 8;
     if (cfg == 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 256, 4, 2, 4, 2, MODE>), dim3(blocks), dim3(512), 0, stream,
-                           a);
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 256, 4, 2, kPrefillStages, kPrefillRowB, 2, MODE>),
+                           dim3(blocks), dim3(512), 0, stream, a);
     else
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 16, 8, 1, 8, 1, MODE>), dim3(blocks), dim3(512), 0, stream,
-                           a);
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 16, 8, 1, kDecodeStages, kDecodeRowB, 1, MODE>), dim3(blocks),
+                           dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ def test_workspace_size_grows_with_tokens(lib):
     (dict(dtype=7), B.INKLING_ERR_UNSUPPORTED),
     (dict(out_dtype=3), B.INKLING_ERR_UNSUPPORTED),
     (dict(hidden=96), B.INKLING_ERR_UNSUPPORTED),          # hidden % 64
-    (dict(intermediate=48), B.INKLING_ERR_UNSUPPORTED),    # intermediate % 32
+    (dict(intermediate=96), B.INKLING_ERR_UNSUPPORTED),    # intermediate % 64
     (dict(n_routed=600, top_k=2), B.INKLING_ERR_UNSUPPORTED),
     (dict(n_routed=64, top_k=33), B.INKLING_ERR_UNSUPPORTED),
     (dict(n_shared=17), B.INKLING_ERR_UNSUPPORTED),
