@@ -24,7 +24,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
     int ksplit, W, cfg, bm, max_tiles;
     size_t zpart, topk_idx, topk_w, shared_g, masks, prefix, counts, offsets, tiles, num_tiles;
-    size_t sorted_slots, row_token, row_gamma, pos, act_r, act_sh, y, total;
+    size_t sorted_slots, row_token, row_gamma, pos, act_r, act_sh, y, ysh, total;
 };
 
 int check_dims(const inkling_moe_dims_t* d) {
@@ -77,6 +77,7 @@ Layout make_layout(const inkling_moe_dims_t* d) {
     L.act_r = take((size_t)T * k * I * es);
     L.act_sh = take((size_t)T * S * I * es);
     L.y = take((size_t)T * k * H * sizeof(float));
+    L.ysh = take((size_t)T * (S > 0 ? H : 0) * sizeof(float));
     L.total = o;
     return L;
 }
@@ -224,20 +225,24 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
     p.num_tiles = rb.num_tiles;
     p.offsets = rb.offsets;
     p.row_token = rb.row_token;
+    p.row_slot = rb.sorted_slots;
     p.row_gamma = rb.row_gamma;
     p.shared_g = rb.shared_g;
     p.pos = rb.pos;
     p.act_r = at<void>(workspace, L.act_r);
     p.act_sh = at<void>(workspace, L.act_sh);
     p.y = at<void>(workspace, L.y);
+    p.ysh = at<void>(workspace, L.ysh);
     p.out = out;
     p.max_routed_tiles = L.max_tiles;
     HIP_TRY(launch_gate_up(p, s));
     HIP_TRY(mark(4, s));
     HIP_TRY(launch_down_routed(p, s));
     HIP_TRY(mark(5, s));
-    HIP_TRY(launch_down_shared_combine(p, s));
+    HIP_TRY(launch_down_shared(p, s));
     HIP_TRY(mark(6, s));
+    HIP_TRY(launch_combine(p, s));
+    HIP_TRY(mark(7, s));
     return INKLING_OK;
 }
 

@@ -1,4 +1,5 @@
-// Grouped expert GEMMs of the Inkling MoE on gfx950 matrix cores.
+// Grouped expert GEMMs of the Inkling MoE on gfx950 matrix cores, and the
+// combine of their outputs.
 //
 // Every expert product here is out[row][n] = sum_k W[n][k] * X[row][k] with
 // both operands K-contiguous (nn.Linear weights [out, in] and row-major token
@@ -9,17 +10,18 @@
 // interleaved layout (inkling_swiglu on the Inkling layers page: ::2 gate,
 // 1::2 up), so SwiGLU and the routing-weight scale are applied in registers.
 //
-// Three launches per forward:
+// Launches per forward:
 //   gate_up       routed tiles (rows gathered through the expert-sorted token
 //                 list, scaled by that slot's gamma) and shared tiles (all
 //                 tokens against the S shared experts concatenated along N,
 //                 scaled by the token's shared gamma) -> act_r, act_sh;
-//   down routed   act_r rows of each expert -> y (one fp32 row per routed slot);
-//   down shared   act_sh [T][S*I] against the shared down weights
-//                 concatenated along K (the sum over shared experts happens in
-//                 the reduction), with the routed rows y[pos(t, i)] added in the
-//                 epilogue -> out.  With S = 0 the reduction is empty and the
-//                 kernel is the combine alone.
+//   down routed   act_r rows of each expert -> y, one fp32 row per routed slot
+//                 t*k + i (rows of a token are adjacent);
+//   down shared   act_sh [T][S*I] against the shared down weights concatenated
+//                 along K, so the sum over shared experts happens inside the
+//                 reduction -> ysh [T][H] fp32;
+//   combine       out[t] = ysh[t] + sum_i y[t*k + i], rounded once.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -29,7 +31,7 @@ namespace inkling {
 
 namespace {
 
-enum { kModeGateUp = 0, kModeDown = 1, kModeDownCombine = 2 };
+enum { kModeGateUp = 0, kModeDown = 1 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
@@ -43,12 +45,11 @@ struct GemmKArgs {
     const int32_t* num_tiles;
     const int32_t* offsets;
     const int32_t* row_token;
+    const int32_t* row_slot;   // sorted row -> slot t*k + i
     const float* row_gamma;
     const float* shared_g;
-    const int32_t* pos;
-    const float* y;
-    void* out_routed;
-    void* out_shared;
+    void* out_routed;          // gate_up: act_r [T*k][I] (sorted rows); down: y [T*k][H] fp32 (slot rows)
+    void* out_shared;          // gate_up: act_sh [T][S*I]; down: ysh [T][H] fp32
     int T, H, I, S, k;
     int K_r, N_r, ntn_r;    // routed problem: K, N per expert, N tiles
     int K_s, N_s, ntn_s;    // shared problem
@@ -120,18 +121,6 @@ __device__ __forceinline__ void barrier_keep_loads() {
     __asm__ volatile("s_barrier" ::: "memory");
 }
 
-// Logical tile of block `bid`: blocks are dealt to the 8 XCDs round-robin, so
-// each XCD receives a contiguous range of logical tiles (neighbouring tiles
-// share operands through that XCD's L2).  Returns -1 for blocks beyond the
-// device-side tile count.
-__device__ __forceinline__ int xcd_tile(int bid, int nb_real) {
-    const int per = (nb_real + 7) >> 3;
-    const int loc = bid >> 3;
-    if (loc >= per) return -1;
-    const int L = (bid & 7) * per + loc;
-    return L < nb_real ? L : -1;
-}
-
 // Grouped ordering of an (MT x NT) tile grid: consecutive ids cycle over up to
 // GM row tiles, then advance the column tile.
 template <int GM>
@@ -153,20 +142,68 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// BN weight rows x BM token rows per workgroup; WN x WM waves (8, two per
-// SIMD); STAGES LDS pipeline stages of ROWB bytes of K per row, filled by
-// direct global->LDS loads.  TE: operand and intermediate type; TO: type of
-// the layer output (combine mode).
+// One output tile: BN weight rows from n0 x up to BM token rows.
+template <typename TE>
+struct Tile {
+    bool is_shared;
+    int K, N, seg, n0, rows_valid, grow0, t0;
+    const TE* A;
+    const TE* B;
+};
+
+template <typename TE, int BM, int GM>
+__device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int BN) {
+    Tile<TE> t;
+    t.is_shared = L < a.shared_blocks;
+    t.grow0 = 0;
+    t.t0 = 0;
+    if (t.is_shared) {
+        int mt, nt;
+        grouped<GM>(L, a.shared_mtiles, a.ntn_s, mt, nt);
+        t.t0 = mt * BM;
+        t.rows_valid = min(BM, a.T - t.t0);
+        t.n0 = nt * BN;
+        t.K = a.K_s;
+        t.N = a.N_s;
+        t.seg = a.seg_s;
+        t.A = reinterpret_cast<const TE*>(a.A_shared);
+        t.B = reinterpret_cast<const TE*>(a.B_shared);
+    } else {
+        int ti, nt;
+        grouped<GM>(L - a.shared_blocks, *a.num_tiles, a.ntn_r, ti, nt);
+        const RoutedTile tl = a.tiles[ti];
+        const int base = a.offsets[tl.expert];
+        t.rows_valid = min(BM, a.offsets[tl.expert + 1] - base - tl.row_start);
+        t.grow0 = base + tl.row_start;
+        t.n0 = nt * BN;
+        t.K = a.K_r;
+        t.N = a.N_r;
+        t.seg = a.K_r;
+        t.A = reinterpret_cast<const TE*>(a.A_routed) + (size_t)tl.expert * a.N_r * a.K_r;
+        t.B = reinterpret_cast<const TE*>(a.B_routed);
+    }
+    return t;
+}
+
+// Persistent grouped GEMM.  A workgroup owns a contiguous range of grouped
+// tiles on its XCD (blocks are dealt to the 8 XCDs round-robin, so workgroups
+// that run side by side on one XCD share that range's operands through its L2)
+// and walks the range with stride = workgroups per XCD.  BN weight rows x BM
+// token rows per tile; WN x WM waves (8, two per SIMD); STAGES LDS pipeline
+// stages of ROWB bytes of K per row, filled by direct global->LDS loads.  TE:
+// operand and intermediate type.
 //
 // Each stage is its own __shared__ array and the K loop is unrolled by STAGES,
 // so every LDS read and every LDS-DMA target is a distinct, statically known
 // object: the compiler then needs no wait on in-flight DMA before reading a
-// stage that is already complete.
-template <typename TE, typename TO, int BN, int BM, int WN, int WM, int STAGES, int ROWB, int GM, int MODE>
+// stage that is already complete.  The first stages of the next tile are
+// loaded before the epilogue of the current one, so the epilogue's stores and
+// SwiGLU arithmetic overlap the next tile's load latency.
+template <typename TE, int BN, int BM, int WN, int WM, int STAGES, int ROWB, int GM, int MODE>
 __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs a) {
     constexpr int NW = WN * WM;                     // waves per workgroup
     static_assert(NW == 8, "eight waves: two per SIMD");
-    static_assert(STAGES >= 2 && STAGES <= 8, "stages");
+    static_assert(STAGES >= 2 && STAGES <= 8 && STAGES % 2 == 0, "even stage count");
     static_assert(ROWB == 64 || ROWB == 128, "64 or 128 bytes of K per row and stage");
     constexpr int CH = ROWB / 16;                   // 16-byte chunks per row and stage
     constexpr int KS = ROWB / 64;                   // MFMA k-steps per stage (64 bytes of K each)
@@ -206,71 +243,51 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) wave index
     const int wn0 = (wv % WN) * WTN, wm = wv / WN;              // token blocks wm, wm+WM, ...
+    const int rl = lane & 15;
 
-    // ---- which tile -------------------------------------------------------
+    // ---- this workgroup's tiles ---------------------------------------------
     const int nb_real = a.shared_blocks + (a.has_routed ? (*a.num_tiles) * a.ntn_r : 0);
-    const int L = xcd_tile(blockIdx.x, nb_real);
-    if (L < 0) return;
-    const bool is_shared = L < a.shared_blocks;
-    int K, N, seg, n0, rows_valid, grow0 = 0, t0 = 0;
-    const TE* A;
-    const TE* Bsrc;
-    if (is_shared) {
-        int mt, nt;
-        grouped<GM>(L, a.shared_mtiles, a.ntn_s, mt, nt);
-        t0 = mt * BM;
-        rows_valid = min(BM, a.T - t0);
-        n0 = nt * BN;
-        K = a.K_s;
-        N = a.N_s;
-        seg = a.seg_s;
-        A = reinterpret_cast<const TE*>(a.A_shared);
-        Bsrc = reinterpret_cast<const TE*>(a.B_shared);
-    } else {
-        int ti, nt;
-        grouped<GM>(L - a.shared_blocks, *a.num_tiles, a.ntn_r, ti, nt);
-        const RoutedTile tl = a.tiles[ti];
-        const int base = a.offsets[tl.expert];
-        rows_valid = min(BM, a.offsets[tl.expert + 1] - base - tl.row_start);
-        grow0 = base + tl.row_start;
-        n0 = nt * BN;
-        K = a.K_r;
-        N = a.N_r;
-        seg = a.K_r;
-        A = reinterpret_cast<const TE*>(a.A_routed) + (size_t)tl.expert * a.N_r * a.K_r;
-        Bsrc = reinterpret_cast<const TE*>(a.B_routed);
-    }
+    const int per = (nb_real + 7) >> 3;
+    const int nloc = gridDim.x >> 3;
+    const int L_end = min(((int)(blockIdx.x & 7) + 1) * per, nb_real);
+    int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (L >= L_end) return;
 
-    // ---- load sources ------------------------------------------------------
+    // ---- load sources and the stage issue -------------------------------------
     // LDS rows are ROWB bytes; the 16-byte chunk c of row r sits at chunk
     // position c ^ sw(r), which makes the fragment reads below conflict-free.
     // A wave load fills RPL rows: lane -> row lane / CH, chunk position lane % CH.
     auto sw = [](int r) { return CH == 4 ? ((r >> 1) & 3) : (r & 7); };
     const int lr = lane / CH, lp = lane % CH;
     const TE* a_src[A_PW];
-#pragma unroll
-    for (int q = 0; q < A_PW; ++q) {
-        const int r = RPL * (wv + NW * q) + lr;
-        a_src[q] = A + (size_t)min(n0 + r, N - 1) * seg + (lp ^ sw(r)) * EPC;   // rows past N re-read row N-1
-    }
     const TE* b_src[B_PW];
+    int a_k = 0, next_k = 0, rows_valid_ld = 1, seg_ld = 1;
+    size_t a_seg = 0, a_seg_step = 0;
+    auto setup = [&](const Tile<TE>& t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < B_PW; ++q) {
-        const int r = RPL * (wv + NW * q) + lr;
-        const int rr = min(r, rows_valid - 1);   // rows past the end re-read the last valid row
-        size_t row;
-        if (is_shared) row = (size_t)(t0 + rr);
-        else if (MODE == kModeGateUp) row = (size_t)a.row_token[grow0 + rr];
-        else row = (size_t)(grow0 + rr);
-        b_src[q] = Bsrc + row * K + (lp ^ sw(r)) * EPC;
-    }
-
+        for (int q = 0; q < A_PW; ++q) {
+            const int r = RPL * (wv + NW * q) + lr;
+            a_src[q] = t.A + (size_t)min(t.n0 + r, t.N - 1) * t.seg + (lp ^ sw(r)) * EPC;   // rows past N re-read N-1
+        }
+#pragma unroll
+        for (int q = 0; q < B_PW; ++q) {
+            const int r = RPL * (wv + NW * q) + lr;
+            const int rr = min(r, t.rows_valid - 1);   // rows past the end re-read the last valid row
+            size_t row;
+            if (t.is_shared) row = (size_t)(t.t0 + rr);
+            else if (MODE == kModeGateUp) row = (size_t)a.row_token[t.grow0 + rr];
+            else row = (size_t)(t.grow0 + rr);
+            b_src[q] = t.B + row * t.K + (lp ^ sw(r)) * EPC;
+        }
+        a_k = 0;
+        next_k = 0;
+        a_seg = 0;
+        a_seg_step = (size_t)t.N * t.seg;
+        seg_ld = t.seg;
+        rows_valid_ld = t.rows_valid;
+    };
     // K offset of A at the next stage to issue: A rows are read in segments of
     // `seg` columns (the shared down projection concatenates S experts along K)
-    int a_k = 0;
-    size_t a_seg = 0;
-    const size_t a_seg_step = (size_t)N * seg;
-    int next_k = 0;
     auto issue = [&](auto S_) __attribute__((always_inline)) {
         uint8_t* __restrict__ sb = stage(S_);
         const size_t aoff = a_seg + a_k;
@@ -281,15 +298,45 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 #pragma unroll
         for (int q = 0; q < B_PW; ++q) {
             const int qi = wv + NW * q;
-            if (qi < B_INS && RPL * qi < rows_valid)
+            if (qi < B_INS && RPL * qi < rows_valid_ld)
                 __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[q] + next_k),
                                                  (lds_void_t*)(sb + A_BYTES + qi * 1024), 16, 0, 0);
         }
         next_k += BK;
         a_k += BK;
-        if (a_k == seg) {
+        if (a_k == seg_ld) {
             a_k = 0;
             a_seg += a_seg_step;
+        }
+    };
+    auto issue_first = [&](int nk) __attribute__((always_inline)) {
+        static_for<0, STAGES>([&](auto S_) {
+            if (decltype(S_)::value < nk) issue(S_);
+        });
+    };
+
+    // per-row epilogue data, loaded when a tile starts (used after its K loop)
+    float ep_g0[FM], ep_g1[FM];   // gate_up: gamma of the row (routed) / of the wave's first and last shared expert
+    int ep_row[FM];               // down: output row (slot for routed tiles, token for shared tiles)
+    int ep_s0 = 0;                // gate_up shared: expert of the wave's first weight row
+    auto prefetch_epilogue = [&](const Tile<TE>& t) __attribute__((always_inline)) {
+        const int s0 = min((t.n0 + wn0) / (2 * a.I), max(a.S - 1, 0));
+        const int s1 = min((t.n0 + wn0 + WTN - 1) / (2 * a.I), max(a.S - 1, 0));
+        ep_s0 = s0;
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = min(16 * (WM * j + wm) + rl, t.rows_valid - 1);
+            if (MODE == kModeGateUp) {
+                if (t.is_shared) {
+                    ep_g0[j] = a.shared_g[(size_t)(t.t0 + m) * a.S + s0];
+                    ep_g1[j] = a.shared_g[(size_t)(t.t0 + m) * a.S + s1];
+                } else {
+                    ep_g0[j] = a.row_gamma[t.grow0 + m];
+                    ep_g1[j] = 0.f;
+                }
+            } else {
+                ep_row[j] = t.is_shared ? t.t0 + m : a.row_slot[t.grow0 + m];
+            }
         }
     };
 
@@ -299,11 +346,9 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
     // fragment rows: A rows wn0 + 16i + rl, B rows 16*(WM*j + wm) + rl; 16-row
     // blocks start at multiples of 8 rows, so sw(row) = sw(rl) throughout.
     // In k-step s a lane feeds logical chunk 4s + lane/16 to the MFMA.
-    const int rl = lane & 15;
     int a_rd[KS], b_rd[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -322,18 +367,15 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     //   reads -> MFMAs of this half-step.
     // Before the stage's last half-step (all its reads done): wait for this
     // wave's DMA of stage kt+1, barrier, DMA stage kt+STAGES into the buffer
-    // just freed, then read the first half-step of stage kt+1.
-    auto kloop = [&](auto NJ_) __attribute__((always_inline)) {
+    // just freed, then read the first half-step of stage kt+1.  The first
+    // STAGES stages of a tile are issued before its K loop.
+    auto kloop = [&](auto NJ_, int nk) __attribute__((always_inline)) {
         constexpr int NJ = decltype(NJ_)::value;
         constexpr int H1 = (NJ + 1) / 2, H2 = NJ - H1;
         constexpr int HS = H2 > 0 ? 2 * KS : KS;    // half-steps per stage
-        static_assert((STAGES % 2) == 0, "even stage count keeps buffer parity static");
         // fragments double-buffered by the parity of the global k-step (A) and
         // half-step (B) index; with STAGES even both parities are compile-time
         uint4 fa[2][FN], fb[2][H1];
-        static_for<0, STAGES>([&](auto S_) {
-            if (decltype(S_)::value < nk) issue(S_);
-        });
         if (STAGES - 1 < nk) wait_vmcnt<(STAGES - 1) * A_PW>();
         else wait_vmcnt<0>();
         barrier_keep_loads();
@@ -402,96 +444,159 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         }
     };
 
-    // token blocks / weight-row blocks of this wave that hold valid rows
-    const int nvb_all = (rows_valid + 15) >> 4;
-    const int nvb = min(FM, max(0, (nvb_all - wm + WM - 1) / WM));
-    const int nvi = min(FN, max(0, (N - n0 - wn0 + 15) >> 4));
-    if constexpr (FM == 1) {
-        kloop(std::integral_constant<int, 1>{});
-    } else {
-        // a wave without valid token rows still runs one block, to take part in the
-        // loads and barriers; nothing of it is stored
-        const int nvb_run = max(nvb, 1);
-        static_for<1, FM + 1>([&](auto P_) {
-            if (nvb_run == decltype(P_)::value) kloop(std::integral_constant<int, decltype(P_)::value>{});
-        });
-    }
+    Tile<TE> cur = decode_tile<TE, BM, GM>(a, L, BN);
+    setup(cur);
+    issue_first(cur.K / BK);
+    prefetch_epilogue(cur);
 
-    // ---- epilogue ----------------------------------------------------------
-    // acc[i][j][r]: output column n = n0 + wn0 + 16i + 4*(lane/16) + r, row m = 16*(WM*j + wm) + lane%16
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int m = 16 * (WM * j + wm) + (lane & 15);
-        if (j >= nvb || m >= rows_valid) continue;
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int n = n0 + wn0 + 16 * i + 4 * (lane >> 4);
-            if (i >= nvi) continue;
-            const f32x4_t v = acc[i][j];
-            if (MODE == kModeGateUp) {
-                if (is_shared) {
-                    const int t = t0 + m;
-                    const int s = n / (2 * a.I);
-                    const float g = a.shared_g[(size_t)t * a.S + s];
-                    TE* o = reinterpret_cast<TE*>(a.out_shared) + (size_t)t * a.S * a.I + (n >> 1);
-                    store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
-                } else {
-                    const int row = grow0 + m;
-                    const float g = a.row_gamma[row];
-                    TE* o = reinterpret_cast<TE*>(a.out_routed) + (size_t)row * a.I + (n >> 1);
-                    store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
-                }
-            } else if (MODE == kModeDown) {
-                // per-slot rows stay fp32 so the output is rounded once, in the combine
-                const int row = grow0 + m;
-                float w[4] = {v[0], v[1], v[2], v[3]};
-                store4<float>(reinterpret_cast<float*>(a.out_routed) + (size_t)row * a.H + n, w);
+    while (true) {
+        const int nk = cur.K / BK;
+        // token blocks / weight-row blocks of this wave that hold valid rows
+        const int nvb_all = (cur.rows_valid + 15) >> 4;
+        const int nvb = min(FM, max(0, (nvb_all - wm + WM - 1) / WM));
+        const int nvi = min(FN, max(0, (cur.N - cur.n0 - wn0 + 15) >> 4));
+        if (nk > 0) {
+            if constexpr (FM == 1) {
+                kloop(std::integral_constant<int, 1>{}, nk);
             } else {
-                const int t = t0 + m;
-                float w[4] = {v[0], v[1], v[2], v[3]};
-                for (int q = 0; q < a.k; ++q) {
-                    const int p = a.pos[(size_t)t * a.k + q];
-                    if (p < 0) continue;
-                    const float4 yv = *reinterpret_cast<const float4*>(a.y + (size_t)p * a.H + n);
-                    w[0] += yv.x; w[1] += yv.y; w[2] += yv.z; w[3] += yv.w;
-                }
-                store4<TO>(reinterpret_cast<TO*>(a.out_shared) + (size_t)t * a.H + n, w);
+                // a wave without valid token rows still runs one block, to take part
+                // in the loads and barriers; nothing of it is stored
+                const int nvb_run = max(nvb, 1);
+                static_for<1, FM + 1>([&](auto P_) {
+                    if (nvb_run == decltype(P_)::value) kloop(std::integral_constant<int, decltype(P_)::value>{}, nk);
+                });
             }
         }
+
+        // all waves are done reading the stages: start loading the next tile
+        L += nloc;
+        const bool has_next = L < L_end;
+        wait_lgkmcnt0();
+        barrier_keep_loads();
+        Tile<TE> nxt = cur;
+        if (has_next) {
+            nxt = decode_tile<TE, BM, GM>(a, L, BN);
+            setup(nxt);
+            issue_first(nxt.K / BK);
+        }
+
+        // ---- epilogue of the current tile ----------------------------------
+        // acc[i][j][r]: output column n = n0 + wn0 + 16i + 4*(lane/16) + r,
+        // token row m = 16*(WM*j + wm) + lane%16
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = 16 * (WM * j + wm) + rl;
+            if (j < nvb && m < cur.rows_valid) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    const int n = cur.n0 + wn0 + 16 * i + 4 * (lane >> 4);
+                    if (i < nvi) {
+                        const f32x4_t v = acc[i][j];
+                        if (MODE == kModeGateUp) {
+                            if (cur.is_shared) {
+                                const int t = cur.t0 + m;
+                                const float g = (n / (2 * a.I) == ep_s0) ? ep_g0[j] : ep_g1[j];
+                                TE* o = reinterpret_cast<TE*>(a.out_shared) + (size_t)t * a.S * a.I + (n >> 1);
+                                store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
+                            } else {
+                                const int row = cur.grow0 + m;
+                                const float g = ep_g0[j];
+                                TE* o = reinterpret_cast<TE*>(a.out_routed) + (size_t)row * a.I + (n >> 1);
+                                store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
+                            }
+                        } else {
+                            // fp32 rows: the layer output is rounded once, in the combine
+                            float w[4] = {v[0], v[1], v[2], v[3]};
+                            float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed);
+                            store4<float>(o + (size_t)ep_row[j] * a.H + n, w);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (!has_next) break;
+        cur = nxt;
+        prefetch_epilogue(cur);
+    }
+}
+
+// out[t][h] = ysh[t][h] (if S > 0) + sum over i < k of y[t*k + i][h] for the
+// slots that were dispatched (pos >= 0), in fp32, rounded once to TO.
+// One thread per 4 consecutive columns of one token; H % 4 == 0.
+template <typename TO>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
+                                                      const int32_t* __restrict__ pos, TO* __restrict__ out, int T,
+                                                      int H, int k) {
+    const int hq = H >> 2;
+    const size_t total = (size_t)T * hq;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(idx / hq);
+        const int c = (int)(idx - (size_t)t * hq) * 4;
+        float4 s = ysh ? *reinterpret_cast<const float4*>(ysh + (size_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int32_t* pt = pos + (size_t)t * k;
+        const float* yt = y + (size_t)t * k * H + c;
+#pragma unroll 4
+        for (int i = 0; i < k; ++i) {
+            if (pt[i] >= 0) {
+                const float4 v = *reinterpret_cast<const float4*>(yt + (size_t)i * H);
+                s.x += v.x;
+                s.y += v.y;
+                s.z += v.z;
+                s.w += v.w;
+            }
+        }
+        float w[4] = {s.x, s.y, s.z, s.w};
+        store4<TO>(out + (size_t)t * H + c, w);
     }
 }
 
 // ---- tile configurations ---------------------------------------------------
 // cfg 0 (many rows per expert): 256 weight rows x 256 tokens, 8 waves (two per
 //       SIMD) as 4 along the weight rows x 2 along the tokens, each 64 rows x
-//       128 tokens (token blocks interleaved), 4 stages (128 KB LDS).
+//       128 tokens (token blocks interleaved), 2 stages of 128-byte rows.
 // cfg 1 (few rows per expert, decode): 256 weight rows x 16 tokens, 8 waves
-//       along the weight rows, 8 stages.
+//       along the weight rows, 4 stages.
 constexpr int kBN = 256;
 constexpr int kPrefillStages = 2, kPrefillRowB = 128;
 constexpr int kDecodeStages = 4, kDecodeRowB = 128;
 
-template <typename TE, typename TO, int MODE>
-hipError_t launch_mode(int cfg, const GemmKArgs& a, int blocks, hipStream_t stream) {
-    if (blocks <= 0) return hipSuccess;
-    blocks = (blocks + 7) / 8 * 8;
+int num_cus() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+template <typename TE, int MODE>
+hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t stream) {
+    if (max_tiles <= 0) return hipSuccess;
+    // persistent: at most one workgroup per CU (LDS), a multiple of the 8 XCDs
+    int grid = std::min(max_tiles, num_cus());
+    grid = (grid + 7) / 8 * 8;
     if (cfg == 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 256, 4, 2, kPrefillStages, kPrefillRowB, 2, MODE>),
-                           dim3(blocks), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 256, 4, 2, kPrefillStages, kPrefillRowB, 2, MODE>), dim3(grid),
+                           dim3(512), 0, stream, a);
     else
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, TO, 256, 16, 8, 1, kDecodeStages, kDecodeRowB, 1, MODE>), dim3(blocks),
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 16, 8, 1, kDecodeStages, kDecodeRowB, 1, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t launch_dispatch(const MoeGemmParams& p, const GemmKArgs& a, int blocks, hipStream_t stream) {
-    if (MODE == kModeDownCombine && p.out_dtype != p.dtype) {
-        if (p.dtype == 1) return launch_mode<bf16_t, float, MODE>(p.cfg, a, blocks, stream);
-        return launch_mode<float, bf16_t, MODE>(p.cfg, a, blocks, stream);
-    }
-    if (p.dtype == 1) return launch_mode<bf16_t, bf16_t, MODE>(p.cfg, a, blocks, stream);
-    return launch_mode<float, float, MODE>(p.cfg, a, blocks, stream);
+hipError_t launch_dispatch(const MoeGemmParams& p, const GemmKArgs& a, int max_tiles, hipStream_t stream) {
+    if (p.dtype == 1) return launch_mode<bf16_t, MODE>(p.cfg, a, max_tiles, stream);
+    return launch_mode<float, MODE>(p.cfg, a, max_tiles, stream);
 }
 
 GemmKArgs base_args(const MoeGemmParams& p) {
@@ -500,10 +605,9 @@ GemmKArgs base_args(const MoeGemmParams& p) {
     a.num_tiles = p.num_tiles;
     a.offsets = p.offsets;
     a.row_token = p.row_token;
+    a.row_slot = p.row_slot;
     a.row_gamma = p.row_gamma;
     a.shared_g = p.shared_g;
-    a.pos = p.pos;
-    a.y = reinterpret_cast<const float*>(p.y);
     a.T = p.T;
     a.H = p.H;
     a.I = p.I;
@@ -541,8 +645,7 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     a.seg_s = p.H;
     a.shared_mtiles = (p.T + bm - 1) / bm;
     a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
-    const int blocks = a.shared_blocks + p.max_routed_tiles * a.ntn_r;
-    return launch_dispatch<kModeGateUp>(p, a, blocks, stream);
+    return launch_dispatch<kModeGateUp>(p, a, a.shared_blocks + p.max_routed_tiles * a.ntn_r, stream);
 }
 
 hipError_t launch_down_routed(const MoeGemmParams& p, hipStream_t stream) {
@@ -558,16 +661,16 @@ hipError_t launch_down_routed(const MoeGemmParams& p, hipStream_t stream) {
     a.shared_mtiles = 1;
     a.ntn_s = 1;
     a.seg_s = 1;
-    const int blocks = p.max_routed_tiles * a.ntn_r;
-    return launch_dispatch<kModeDown>(p, a, blocks, stream);
+    return launch_dispatch<kModeDown>(p, a, p.max_routed_tiles * a.ntn_r, stream);
 }
 
-hipError_t launch_down_shared_combine(const MoeGemmParams& p, hipStream_t stream) {
+hipError_t launch_down_shared(const MoeGemmParams& p, hipStream_t stream) {
+    if (p.S == 0) return hipSuccess;
     GemmKArgs a = base_args(p);
     const int bm = gemm_cfg_bm(p.cfg);
     a.A_shared = p.wsh_d;
     a.B_shared = p.act_sh;
-    a.out_shared = p.out;
+    a.out_shared = p.ysh;
     a.K_s = p.S * p.I;
     a.N_s = p.H;
     a.ntn_s = (p.H + kBN - 1) / kBN;
@@ -575,7 +678,21 @@ hipError_t launch_down_shared_combine(const MoeGemmParams& p, hipStream_t stream
     a.shared_mtiles = (p.T + bm - 1) / bm;
     a.shared_blocks = a.shared_mtiles * a.ntn_s;
     a.has_routed = 0;
-    return launch_dispatch<kModeDownCombine>(p, a, a.shared_blocks, stream);
+    return launch_dispatch<kModeDown>(p, a, a.shared_blocks, stream);
+}
+
+hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream) {
+    const size_t items = (size_t)p.T * (p.H / 4);
+    const int blocks = (int)std::min<size_t>((items + 255) / 256, (size_t)num_cus() * 16);
+    const float* ysh = p.S > 0 ? reinterpret_cast<const float*>(p.ysh) : nullptr;
+    const float* y = reinterpret_cast<const float*>(p.y);
+    if (p.out_dtype == 1)
+        hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
+                           reinterpret_cast<bf16_t*>(p.out), p.T, p.H, p.k);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
+                           reinterpret_cast<float*>(p.out), p.T, p.H, p.k);
+    return hipGetLastError();
 }
 
 }  // namespace inkling

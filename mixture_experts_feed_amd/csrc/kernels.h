@@ -30,9 +30,9 @@ hipError_t launch_scatter(const int32_t* topk_idx, const float* topk_w, const ui
                           int32_t* sorted_slots, int32_t* row_token, float* row_gamma, int32_t* pos,
                           hipStream_t stream);
 
-// ---- grouped GEMMs (gemm.hip) --------------------------------------------
+// ---- grouped GEMMs and combine (gemm.hip) ---------------------------------
 struct MoeGemmParams {
-    int dtype;       // 0 f32, 1 bf16: x, weights, act, y
+    int dtype;       // 0 f32, 1 bf16: x, weights, act
     int out_dtype;   // 0 f32, 1 bf16: out
     int cfg;         // tile configuration id (see gemm.hip)
     int T, H, E, S, I, k;
@@ -44,13 +44,15 @@ struct MoeGemmParams {
     const RoutedTile* tiles;
     const int32_t* num_tiles;
     const int32_t* offsets;
-    const int32_t* row_token;
-    const float* row_gamma;
+    const int32_t* row_token;   // sorted row -> token
+    const int32_t* row_slot;    // sorted row -> slot t*k + i
+    const float* row_gamma;     // sorted row -> gamma
     const float* shared_g;
-    const int32_t* pos;
-    void* act_r;   // [T*k][I]
+    const int32_t* pos;         // slot -> sorted row, -1 if not dispatched
+    void* act_r;   // [T*k][I] sorted rows
     void* act_sh;  // [T][S*I]
-    void* y;       // [T*k][H] fp32
+    void* y;       // [T*k][H] fp32, slot rows
+    void* ysh;     // [T][H] fp32
     void* out;     // [T][H]
     int max_routed_tiles;
 };
@@ -58,6 +60,7 @@ int gemm_cfg_for(int dtype, int T, int H, int E, int k, int I);
 int gemm_cfg_bm(int cfg);
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
 hipError_t launch_down_routed(const MoeGemmParams& p, hipStream_t stream);
-hipError_t launch_down_shared_combine(const MoeGemmParams& p, hipStream_t stream);
+hipError_t launch_down_shared(const MoeGemmParams& p, hipStream_t stream);
+hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream);
 
 }  // namespace inkling
