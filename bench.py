@@ -17,8 +17,10 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +29,13 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes per launch of the gate_up kernel, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE), scaled by the copy-kernel factor; valid only while
+# the GEMM sources hash to the value recorded beside them.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gate_up_prefill_h6144_traffic.md")
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_feed_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
 
 
 def log(msg):
@@ -86,6 +95,41 @@ def run_timed(torch, B, call, steps, warmup, events: HipEvents):
     return (t1 - t0) * 1e3 / steps, stage.mean(axis=0), stage
 
 
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Measured HBM bytes per gate_up launch, or None when the kernel source
+    changed since the counters were taken (or none were taken)."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m_h = re.search(r"^source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
+    if not m_h or not m_b or m_h.group(1) != gemm_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def copy_calibration(torch, mib):
+    """A plain device-to-device copy of `mib` MiB (read mib, write mib), for
+    scaling FETCH_SIZE / WRITE_SIZE to bytes."""
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {mib} MiB three times")
+
+
 def cpu_baseline(inp, w, n_tokens):
     """The fp64 oracle on the first n_tokens tokens of the same workload."""
     import torch
@@ -128,7 +172,9 @@ def main():
     ap.add_argument("--decode-workload", default="decode_h6144")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,6 +190,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = "cuda:0"
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
     B.load()
     w = wl.WORKLOADS[args.workload]
     log(f"[bench] drawing inputs for {w.name}")
@@ -174,7 +223,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     roofline = {"kernel": "moe_gemm_kernel gate_up (routed + shared, SwiGLU epilogue)", "bound": "mfma",
                 "achieved": round(gu_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(gu_tflops / peak, 4), "traffic": None,
+                "frac": round(gu_tflops / peak, 4), "traffic": recorded_traffic(),
                 "per_launch": {"flops": gu_flops, "avg_ms": round(gu_ms, 4)}}
 
     result = {
