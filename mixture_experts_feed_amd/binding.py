@@ -25,8 +25,8 @@ INKLING_BF16 = 1
 
 EXPORTED = ("inkling_moe_workspace_size", "inkling_moe_route", "inkling_moe_forward",
             "inkling_moe_strerror", "inkling_moe_last_hip_error", "inkling_moe_set_stage_events")
-INKLING_STAGE_EVENTS = 8
-STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down_routed", "down_shared", "combine")
+INKLING_STAGE_EVENTS = 7
+STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "combine")
 
 
 class Dims(ctypes.Structure):

@@ -237,12 +237,10 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
     p.max_routed_tiles = L.max_tiles;
     HIP_TRY(launch_gate_up(p, s));
     HIP_TRY(mark(4, s));
-    HIP_TRY(launch_down_routed(p, s));
+    HIP_TRY(launch_down(p, s));
     HIP_TRY(mark(5, s));
-    HIP_TRY(launch_down_shared(p, s));
-    HIP_TRY(mark(6, s));
     HIP_TRY(launch_combine(p, s));
-    HIP_TRY(mark(7, s));
+    HIP_TRY(mark(6, s));
     return INKLING_OK;
 }
 

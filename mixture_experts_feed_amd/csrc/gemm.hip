@@ -169,12 +169,21 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
         t.A = reinterpret_cast<const TE*>(a.A_shared);
         t.B = reinterpret_cast<const TE*>(a.B_shared);
     } else {
-        int ti, nt;
-        grouped<GM>(L - a.shared_blocks, *a.num_tiles, a.ntn_r, ti, nt);
-        const RoutedTile tl = a.tiles[ti];
-        const int base = a.offsets[tl.expert];
-        t.rows_valid = min(BM, a.offsets[tl.expert + 1] - base - tl.row_start);
-        t.grow0 = base + tl.row_start;
+        // The blocks of expert e are [first tile of e, last + 1) x ntn_r; they are
+        // walked column-major (all row tiles of e for weight tile 0, then 1, ...)
+        // so the workgroups side by side on an XCD read each weight tile once.
+        const int l0 = L - a.shared_blocks;
+        const RoutedTile tl0 = a.tiles[l0 / a.ntn_r];
+        const int tb = l0 / a.ntn_r - tl0.row_start / BM;   // first tile of the expert
+        const int base = a.offsets[tl0.expert];
+        const int cnt = a.offsets[tl0.expert + 1] - base;
+        const int c = (cnt + BM - 1) / BM;                  // row tiles of the expert
+        const int l = l0 - tb * a.ntn_r;
+        const int nt = l / c;
+        const int row_start = (l - nt * c) * BM;
+        const RoutedTile tl = {tl0.expert, row_start};
+        t.rows_valid = min(BM, cnt - row_start);
+        t.grow0 = base + row_start;
         t.n0 = nt * BN;
         t.K = a.K_r;
         t.N = a.N_r;
@@ -246,11 +255,23 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     const int rl = lane & 15;
 
     // ---- this workgroup's tiles ---------------------------------------------
-    const int nb_real = a.shared_blocks + (a.has_routed ? (*a.num_tiles) * a.ntn_r : 0);
-    const int per = (nb_real + 7) >> 3;
+    // Each XCD takes a contiguous range of blocks holding an eighth of the K
+    // stages (shared and routed blocks differ in K when S*I is concatenated).
+    const int nb_routed = a.has_routed ? (*a.num_tiles) * a.ntn_r : 0;
+    const int nb_real = a.shared_blocks + nb_routed;
+    const long long cost_s = (long long)a.shared_blocks * a.K_s;
+    const long long cost_all = cost_s + (long long)nb_routed * a.K_r;
+    auto range_start = [&](int x) -> int {
+        if (x >= 8) return nb_real;
+        const long long c = cost_all * x / 8;
+        if (c <= 0) return 0;                                   // also K_s == 0 (no shared blocks)
+        if (c <= cost_s) return (int)((c + a.K_s - 1) / a.K_s);
+        return min(nb_real, a.shared_blocks + (int)((c - cost_s + a.K_r - 1) / a.K_r));
+    };
+    const int xcd = blockIdx.x & 7;
     const int nloc = gridDim.x >> 3;
-    const int L_end = min(((int)(blockIdx.x & 7) + 1) * per, nb_real);
-    int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    const int L_end = range_start(xcd + 1);
+    int L = range_start(xcd) + (blockIdx.x >> 3);
     if (L >= L_end) return;
 
     // ---- load sources and the stage issue -------------------------------------
@@ -585,7 +606,7 @@ hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t s
     int grid = std::min(max_tiles, num_cus());
     grid = (grid + 7) / 8 * 8;
     if (cfg == 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 256, 4, 2, kPrefillStages, kPrefillRowB, 2, MODE>), dim3(grid),
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 256, 4, 2, kPrefillStages, kPrefillRowB, 4, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     else
         hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 16, 8, 1, kDecodeStages, kDecodeRowB, 1, MODE>), dim3(grid),
@@ -648,8 +669,9 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     return launch_dispatch<kModeGateUp>(p, a, a.shared_blocks + p.max_routed_tiles * a.ntn_r, stream);
 }
 
-hipError_t launch_down_routed(const MoeGemmParams& p, hipStream_t stream) {
+hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
     GemmKArgs a = base_args(p);
+    const int bm = gemm_cfg_bm(p.cfg);
     a.A_routed = p.w_d;
     a.B_routed = p.act_r;
     a.out_routed = p.y;
@@ -657,28 +679,17 @@ hipError_t launch_down_routed(const MoeGemmParams& p, hipStream_t stream) {
     a.N_r = p.H;
     a.ntn_r = (p.H + kBN - 1) / kBN;
     a.has_routed = 1;
-    a.shared_blocks = 0;
-    a.shared_mtiles = 1;
-    a.ntn_s = 1;
-    a.seg_s = 1;
-    return launch_dispatch<kModeDown>(p, a, p.max_routed_tiles * a.ntn_r, stream);
-}
-
-hipError_t launch_down_shared(const MoeGemmParams& p, hipStream_t stream) {
-    if (p.S == 0) return hipSuccess;
-    GemmKArgs a = base_args(p);
-    const int bm = gemm_cfg_bm(p.cfg);
+    // shared experts: act_sh [T][S*I] against the S down projections concatenated along K
     a.A_shared = p.wsh_d;
     a.B_shared = p.act_sh;
     a.out_shared = p.ysh;
     a.K_s = p.S * p.I;
     a.N_s = p.H;
-    a.ntn_s = (p.H + kBN - 1) / kBN;
+    a.ntn_s = a.ntn_r;
     a.seg_s = p.I;
     a.shared_mtiles = (p.T + bm - 1) / bm;
-    a.shared_blocks = a.shared_mtiles * a.ntn_s;
-    a.has_routed = 0;
-    return launch_dispatch<kModeDown>(p, a, a.shared_blocks, stream);
+    a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
+    return launch_dispatch<kModeDown>(p, a, a.shared_blocks + p.max_routed_tiles * a.ntn_r, stream);
 }
 
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream) {

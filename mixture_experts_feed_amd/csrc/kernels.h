@@ -59,8 +59,8 @@ struct MoeGemmParams {
 int gemm_cfg_for(int dtype, int T, int H, int E, int k, int I);
 int gemm_cfg_bm(int cfg);
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
-hipError_t launch_down_routed(const MoeGemmParams& p, hipStream_t stream);
-hipError_t launch_down_shared(const MoeGemmParams& p, hipStream_t stream);
+// routed (act_r -> y) and shared (act_sh -> ysh) down projections, one launch
+hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream);
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream);
 
 }  // namespace inkling

@@ -23,7 +23,7 @@ What it computes follows the Inkling layers page
 Everything runs in float64 on the exact input values (bf16 and fp32 inputs widen
 to fp64 without error, and their pairwise products are exact in fp64), with
 numpy's matmul, argsort and cumsum as the only library steps.  Readings taken
-where the pages are silent (documented in the design doc):
+where the pages are silent:
   * gate-bank row order: routed rows 0..E-1, shared rows E..E+S-1;
   * top-k order: descending biased score, equal scores -> lower expert index;
   * route_scale * global_scale scales the shared gammas too;
@@ -37,7 +37,7 @@ on tiny inputs, forced exact ties, the closed form sigma/sum(sigma) of the
 log-sigmoid softmax, gammas summing to route_scale*global_scale, the
 interleaved SwiGLU against the de-interleaved textbook form, a one-expert top-1
 MoE against a dense SwiGLU MLP, token independence, expert relabelling, and a
-hand-derived worked example (tests/golden/hand_example.json).  Agreement with
+hand-derived worked example (test_hand_derived_example).  Agreement with
 the HuggingFace InklingTopkRouter or a real checkpoint: parity unpinned (neither
 exists here).
 """

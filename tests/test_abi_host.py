@@ -34,6 +34,12 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_stage_event_count_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+INKLING_STAGE_EVENTS\s+(\d+)", text)
+    assert m and int(m.group(1)) == B.INKLING_STAGE_EVENTS == len(B.STAGES) + 1
+
+
 def _dims(**kw):
     d = dict(T=64, hidden=128, n_routed=8, top_k=2, n_shared=1, intermediate=64, dtype=B.INKLING_BF16,
              out_dtype=B.INKLING_BF16)
