@@ -23,7 +23,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     int ksplit, W, cfg, bm, max_tiles;
-    size_t zpart, topk_idx, topk_w, shared_g, masks, prefix, counts, offsets, tiles, num_tiles;
+    size_t zpart, topk_idx, topk_w, shared_g, masks, prefix, counts, offsets, tiles, num_tiles, round_counters;
     size_t sorted_slots, row_token, row_gamma, pos, act_r, act_sh, y, ysh, total;
 };
 
@@ -70,6 +70,7 @@ Layout make_layout(const inkling_moe_dims_t* d) {
     L.offsets = take((size_t)(E + 1) * 4);
     L.tiles = take((size_t)L.max_tiles * sizeof(RoutedTile));
     L.num_tiles = take(4);
+    L.round_counters = take(kRoundCounters * 4);
     L.sorted_slots = take((size_t)T * k * 4);
     L.row_token = take((size_t)T * k * 4);
     L.row_gamma = take((size_t)T * k * 4);
@@ -133,7 +134,7 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
     int32_t* prefix = at<int32_t>(ws, L.prefix);
     HIP_TRY(launch_build_masks(rb.topk_idx, pad, T, E, k, masks, L.W, s));
     HIP_TRY(launch_scan(masks, L.W, E, prefix, rb.counts, rb.offsets, rb.tiles ? L.bm : 0, rb.tiles, rb.num_tiles,
-                        s));
+                        rb.tiles ? at<int32_t>(ws, L.round_counters) : nullptr, s));
     HIP_TRY(launch_scatter(rb.topk_idx, rb.topk_w, pad, masks, prefix, rb.offsets, T, E, k, L.W, rb.sorted_slots,
                            rb.row_token, rb.row_gamma, rb.pos, s));
     HIP_TRY(mark(3, s));
@@ -235,6 +236,7 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
     p.ysh = at<void>(workspace, L.ysh);
     p.out = out;
     p.max_routed_tiles = L.max_tiles;
+    p.round_counters = at<int32_t>(workspace, L.round_counters);
     HIP_TRY(launch_gate_up(p, s));
     HIP_TRY(mark(4, s));
     HIP_TRY(launch_down(p, s));

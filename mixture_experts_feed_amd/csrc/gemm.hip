@@ -32,6 +32,7 @@ namespace inkling {
 namespace {
 
 enum { kModeGateUp = 0, kModeDown = 1 };
+constexpr int kSpinLimit = 400;   // polls of a tile-round wait (about 100-400 us at most)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
@@ -56,6 +57,7 @@ struct GemmKArgs {
     int seg_s;              // shared A(n, kk) = A_shared + (kk/seg)*N_s*seg + n*seg + kk%seg
     int shared_blocks, shared_mtiles;
     int has_routed;
+    int32_t* round_counter;    // [8]: tiles finished per XCD (zero at launch)
 };
 
 template <typename TE>
@@ -208,11 +210,15 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
 // stage that is already complete.  The first stages of the next tile are
 // loaded before the epilogue of the current one, so the epilogue's stores and
 // SwiGLU arithmetic overlap the next tile's load latency.
-template <typename TE, int BN, int BM, int WN, int WM, int STAGES, int ROWB, int GM, int MODE>
+template <typename TE, int BN, int BM, int WN, int WM, int SA, int SB, int ROWB, int GM, int SYNC, int MODE>
 __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs a) {
     constexpr int NW = WN * WM;                     // waves per workgroup
     static_assert(NW == 8, "eight waves: two per SIMD");
-    static_assert(STAGES >= 2 && STAGES <= 8 && STAGES % 2 == 0, "even stage count");
+    static_assert(SB >= 2 && SA <= 4 && (SA == SB || SA == SB + 1), "weight stages = token stages (+1)");
+    // stages unrolled per K-loop iteration: every weight and token buffer index
+    // repeats, and the fragment double buffers keep a compile-time parity
+    constexpr int U = SA == SB ? SA : SA * SB;
+    static_assert(U % 2 == 0, "even unroll");
     static_assert(ROWB == 64 || ROWB == 128, "64 or 128 bytes of K per row and stage");
     constexpr int CH = ROWB / 16;                   // 16-byte chunks per row and stage
     constexpr int KS = ROWB / 64;                   // MFMA k-steps per stage (64 bytes of K each)
@@ -223,30 +229,34 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     static_assert(FN >= 1 && FM >= 1, "wave tile at least 16x16");
     static_assert(BN % 64 == 0 && BM % 16 == 0, "tile shape");
     constexpr int RPL = 1024 / ROWB;                // rows per 1 KB wave load
-    constexpr int A_BYTES = BN * ROWB, STAGE_BYTES = (BN + BM) * ROWB;
+    constexpr int A_BYTES = BN * ROWB, B_BYTES = BM * ROWB;
     constexpr int A_INS = BN / RPL, B_INS = BM / RPL;   // 1 KB wave loads per stage
     constexpr int A_PW = A_INS / NW, B_PW = (B_INS + NW - 1) / NW;
     static_assert(A_INS % NW == 0, "A loads spread evenly over the waves");
     constexpr int SMALL = 16;
-    // distinct LDS objects per stage (unused ones shrink to SMALL bytes)
-    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGES > 2 ? STAGE_BYTES : SMALL];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGES > 3 ? STAGE_BYTES : SMALL];
-    __shared__ __attribute__((aligned(16))) uint8_t st4[STAGES > 4 ? STAGE_BYTES : SMALL];
-    __shared__ __attribute__((aligned(16))) uint8_t st5[STAGES > 5 ? STAGE_BYTES : SMALL];
-    __shared__ __attribute__((aligned(16))) uint8_t st6[STAGES > 6 ? STAGE_BYTES : SMALL];
-    __shared__ __attribute__((aligned(16))) uint8_t st7[STAGES > 7 ? STAGE_BYTES : SMALL];
-    auto stage = [&](auto S_) -> uint8_t* {
-        constexpr int sidx = decltype(S_)::value;
-        if constexpr (sidx == 0) return st0;
-        else if constexpr (sidx == 1) return st1;
-        else if constexpr (sidx == 2) return st2;
-        else if constexpr (sidx == 3) return st3;
-        else if constexpr (sidx == 4) return st4;
-        else if constexpr (sidx == 5) return st5;
-        else if constexpr (sidx == 6) return st6;
-        else return st7;
+    // distinct LDS objects per weight stage and per token stage (unused ones
+    // shrink to SMALL bytes)
+    __shared__ __attribute__((aligned(16))) uint8_t sa0[A_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sa1[A_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sa2[SA > 2 ? A_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sa3[SA > 3 ? A_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sb0[B_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sb1[B_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sb2[SB > 2 ? B_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sb3[SB > 3 ? B_BYTES : SMALL];
+    auto stage_a = [&](auto S_) -> uint8_t* {
+        constexpr int i = decltype(S_)::value % SA;
+        if constexpr (i == 0) return sa0;
+        else if constexpr (i == 1) return sa1;
+        else if constexpr (i == 2) return sa2;
+        else return sa3;
+    };
+    auto stage_b = [&](auto S_) -> uint8_t* {
+        constexpr int i = decltype(S_)::value % SB;
+        if constexpr (i == 0) return sb0;
+        else if constexpr (i == 1) return sb1;
+        else if constexpr (i == 2) return sb2;
+        else return sb3;
     };
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -270,8 +280,9 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     };
     const int xcd = blockIdx.x & 7;
     const int nloc = gridDim.x >> 3;
+    const int L_beg = range_start(xcd);
     const int L_end = range_start(xcd + 1);
-    int L = range_start(xcd) + (blockIdx.x >> 3);
+    int L = L_beg + (blockIdx.x >> 3);
     if (L >= L_end) return;
 
     // ---- load sources and the stage issue -------------------------------------
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     const int lr = lane / CH, lp = lane % CH;
     const TE* a_src[A_PW];
     const TE* b_src[B_PW];
-    int a_k = 0, next_k = 0, rows_valid_ld = 1, seg_ld = 1;
+    int a_k = 0, b_k = 0, rows_valid_ld = 1, seg_ld = 1;
     size_t a_seg = 0, a_seg_step = 0;
     auto setup = [&](const Tile<TE>& t) __attribute__((always_inline)) {
 #pragma unroll
@@ -301,38 +312,50 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
             b_src[q] = t.B + row * t.K + (lp ^ sw(r)) * EPC;
         }
         a_k = 0;
-        next_k = 0;
+        b_k = 0;
         a_seg = 0;
         a_seg_step = (size_t)t.N * t.seg;
         seg_ld = t.seg;
         rows_valid_ld = t.rows_valid;
     };
-    // K offset of A at the next stage to issue: A rows are read in segments of
-    // `seg` columns (the shared down projection concatenates S experts along K)
-    auto issue = [&](auto S_) __attribute__((always_inline)) {
-        uint8_t* __restrict__ sb = stage(S_);
+    // Weight stage j is issued SA stage boundaries ahead of its use, token stage
+    // j SB ahead (tokens first within a boundary).  A wave's weight loads per
+    // stage are a fixed A_PW; its token loads vary (rows past a ragged tile's
+    // end are not loaded), so every wait counts weight loads only: waiting
+    // until at most n*A_PW loads are outstanding completes everything issued
+    // before the n youngest weight stages.
+    // K offset of A at the next weight stage to issue: A rows are read in
+    // segments of `seg` columns (the shared down projection concatenates S
+    // experts along K).
+    auto issue_a = [&](auto S_) __attribute__((always_inline)) {
+        uint8_t* __restrict__ dst = stage_a(S_);
         const size_t aoff = a_seg + a_k;
 #pragma unroll
         for (int q = 0; q < A_PW; ++q)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + aoff), (lds_void_t*)(sb + (wv + NW * q) * 1024),
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + aoff), (lds_void_t*)(dst + (wv + NW * q) * 1024),
                                              16, 0, 0);
-#pragma unroll
-        for (int q = 0; q < B_PW; ++q) {
-            const int qi = wv + NW * q;
-            if (qi < B_INS && RPL * qi < rows_valid_ld)
-                __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[q] + next_k),
-                                                 (lds_void_t*)(sb + A_BYTES + qi * 1024), 16, 0, 0);
-        }
-        next_k += BK;
         a_k += BK;
         if (a_k == seg_ld) {
             a_k = 0;
             a_seg += a_seg_step;
         }
     };
+    auto issue_b = [&](auto S_) __attribute__((always_inline)) {
+        uint8_t* __restrict__ dst = stage_b(S_);
+#pragma unroll
+        for (int q = 0; q < B_PW; ++q) {
+            const int qi = wv + NW * q;
+            if (qi < B_INS && RPL * qi < rows_valid_ld)
+                __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[q] + b_k), (lds_void_t*)(dst + qi * 1024), 16, 0,
+                                                 0);
+        }
+        b_k += BK;
+    };
     auto issue_first = [&](int nk) __attribute__((always_inline)) {
-        static_for<0, STAGES>([&](auto S_) {
-            if (decltype(S_)::value < nk) issue(S_);
+        static_for<0, SA>([&](auto S_) {
+            constexpr int j = decltype(S_)::value;
+            if (j < SB && j < nk) issue_b(S_);
+            if (j < nk) issue_a(S_);
         });
     };
 
@@ -375,7 +398,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     for (int s = 0; s < KS; ++s) {
         const int cpos = ((4 * s + (lane >> 4)) ^ sw(rl)) << 4;
         a_rd[s] = (wn0 + rl) * ROWB + cpos;
-        b_rd[s] = A_BYTES + (16 * wm + rl) * ROWB + cpos;
+        b_rd[s] = (16 * wm + rl) * ROWB + cpos;
     }
     constexpr int A_STEP = 16 * ROWB;               // bytes between a wave's weight-row blocks
     constexpr int B_STEP = 16 * WM * ROWB;          // bytes between a wave's token blocks
@@ -387,32 +410,35 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     //   wait for the reads issued last half-step -> issue the next half-step's
     //   reads -> MFMAs of this half-step.
     // Before the stage's last half-step (all its reads done): wait for this
-    // wave's DMA of stage kt+1, barrier, DMA stage kt+STAGES into the buffer
-    // just freed, then read the first half-step of stage kt+1.  The first
-    // STAGES stages of a tile are issued before its K loop.
+    // wave's loads of stage kt+1, barrier, load weight stage kt+SA and token
+    // stage kt+SB into the buffers just freed, then read the first half-step
+    // of stage kt+1.  The first SA weight and SB token stages of a tile are
+    // issued before its K loop.
     auto kloop = [&](auto NJ_, int nk) __attribute__((always_inline)) {
         constexpr int NJ = decltype(NJ_)::value;
         constexpr int H1 = (NJ + 1) / 2, H2 = NJ - H1;
         constexpr int HS = H2 > 0 ? 2 * KS : KS;    // half-steps per stage
         // fragments double-buffered by the parity of the global k-step (A) and
-        // half-step (B) index; with STAGES even both parities are compile-time
+        // half-step (B) index; with U even both parities are compile-time
         uint4 fa[2][FN], fb[2][H1];
-        if (STAGES - 1 < nk) wait_vmcnt<(STAGES - 1) * A_PW>();
+        if (SA - 1 < nk) wait_vmcnt<(SA - 1) * A_PW>();
         else wait_vmcnt<0>();
         barrier_keep_loads();
         {
-            const uint8_t* __restrict__ s0 = stage(std::integral_constant<int, 0>{});
+            const uint8_t* __restrict__ s0a = stage_a(std::integral_constant<int, 0>{});
+            const uint8_t* __restrict__ s0b = stage_b(std::integral_constant<int, 0>{});
 #pragma unroll
-            for (int i = 0; i < FN; ++i) fa[0][i] = *reinterpret_cast<const uint4*>(s0 + a_rd[0] + i * A_STEP);
+            for (int i = 0; i < FN; ++i) fa[0][i] = *reinterpret_cast<const uint4*>(s0a + a_rd[0] + i * A_STEP);
 #pragma unroll
-            for (int j = 0; j < H1; ++j) fb[0][j] = *reinterpret_cast<const uint4*>(s0 + b_rd[0] + j * B_STEP);
+            for (int j = 0; j < H1; ++j) fb[0][j] = *reinterpret_cast<const uint4*>(s0b + b_rd[0] + j * B_STEP);
         }
-        for (int kt0 = 0; kt0 < nk; kt0 += STAGES) {
-            static_for<0, STAGES>([&](auto S_) __attribute__((always_inline)) {
+        for (int kt0 = 0; kt0 < nk; kt0 += U) {
+            static_for<0, U>([&](auto S_) __attribute__((always_inline)) {
                 constexpr int sidx = decltype(S_)::value;
                 const int kt = kt0 + sidx;
                 if (kt < nk) {
-                    const uint8_t* __restrict__ sb = stage(S_);
+                    const uint8_t* __restrict__ sba = stage_a(S_);
+                    const uint8_t* __restrict__ sbb = stage_b(S_);
                     static_for<0, HS>([&](auto H_) __attribute__((always_inline)) {
                         constexpr int h = decltype(H_)::value;
                         constexpr int ks = H2 > 0 ? h >> 1 : h;          // k-step of this half-step
@@ -428,28 +454,32 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
                             if constexpr (halfn == 0) {
 #pragma unroll
                                 for (int i = 0; i < FN; ++i)
-                                    fa[acur ^ 1][i] = *reinterpret_cast<const uint4*>(sb + a_rd[ksn] + i * A_STEP);
+                                    fa[acur ^ 1][i] = *reinterpret_cast<const uint4*>(sba + a_rd[ksn] + i * A_STEP);
                             }
                             constexpr int j0 = halfn ? H1 : 0, jn = halfn ? H2 : H1;
 #pragma unroll
                             for (int j = 0; j < jn; ++j)
-                                fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(sb + b_rd[ksn] + (j0 + j) * B_STEP);
+                                fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(sbb + b_rd[ksn] + (j0 + j) * B_STEP);
                         } else {
                             if (kt + 1 < nk) {
-                                // all reads of this stage are done: refill it, start the next stage
-                                if (kt + STAGES - 1 < nk) wait_vmcnt<(STAGES - 2) * A_PW>();
+                                // all reads of this stage are done: wait for stage kt+1
+                                // (SA-2 younger weight stages may stay in flight),
+                                // refill this stage's buffers, start the next stage
+                                if (kt + SA - 1 < nk) wait_vmcnt<(SA - 2) * A_PW>();
                                 else wait_vmcnt<0>();
                                 barrier_keep_loads();
-                                if (kt + STAGES < nk) issue(S_);
-                                constexpr int snext = (sidx + 1) % STAGES;
-                                const uint8_t* __restrict__ sn = stage(std::integral_constant<int, snext>{});
+                                if (kt + SB < nk) issue_b(S_);
+                                if (kt + SA < nk) issue_a(S_);
+                                constexpr int snext = (sidx + 1) % U;
+                                const uint8_t* __restrict__ sna = stage_a(std::integral_constant<int, snext>{});
+                                const uint8_t* __restrict__ snb = stage_b(std::integral_constant<int, snext>{});
                                 constexpr int an = (snext * KS) & 1;     // A buffer of the next stage's k-step 0
 #pragma unroll
                                 for (int i = 0; i < FN; ++i)
-                                    fa[an][i] = *reinterpret_cast<const uint4*>(sn + a_rd[0] + i * A_STEP);
+                                    fa[an][i] = *reinterpret_cast<const uint4*>(sna + a_rd[0] + i * A_STEP);
 #pragma unroll
                                 for (int j = 0; j < H1; ++j)
-                                    fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(sn + b_rd[0] + j * B_STEP);
+                                    fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(snb + b_rd[0] + j * B_STEP);
                             }
                         }
                         __builtin_amdgcn_sched_barrier(0);
@@ -492,6 +522,25 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         // all waves are done reading the stages: start loading the next tile
         L += nloc;
         const bool has_next = L < L_end;
+        if constexpr (SYNC) {
+            // Tile rounds of an XCD: the workgroups that share operands through
+            // its L2 start round r + 1 together, once round r is finished by all
+            // (bounded wait: after kSpinLimit polls the workgroup goes on).
+            if (tid == 0) {
+                int32_t* ctr = a.round_counter + xcd;
+                __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (has_next) {
+                    // tiles in rounds 0..r of this XCD (round r just finished; with a
+                    // next tile, rounds 0..r are all full)
+                    const int done = L - nloc - L_beg;
+                    const int target = done - done % nloc + nloc;
+                    for (int it = 0; it < kSpinLimit; ++it) {
+                        if (__hip_atomic_fetch_add(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+            }
+        }
         wait_lgkmcnt0();
         barrier_keep_loads();
         Tile<TE> nxt = cur;
@@ -583,7 +632,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // cfg 1 (few rows per expert, decode): 256 weight rows x 16 tokens, 8 waves
 //       along the weight rows, 4 stages.
 constexpr int kBN = 256;
-constexpr int kPrefillStages = 2, kPrefillRowB = 128;
+constexpr int kPrefillStagesA = 2, kPrefillStagesB = 2, kPrefillRowB = 128;
+// tile-round rendezvous per XCD: pays off for the long-K gate_up tiles only
+constexpr int kPrefillSyncGateUp = 1, kPrefillSyncDown = 0;
 constexpr int kDecodeStages = 4, kDecodeRowB = 128;
 
 int num_cus() {
@@ -606,10 +657,11 @@ hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t s
     int grid = std::min(max_tiles, num_cus());
     grid = (grid + 7) / 8 * 8;
     if (cfg == 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 256, 4, 2, kPrefillStages, kPrefillRowB, 4, MODE>), dim3(grid),
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 256, 4, 2, kPrefillStagesA, kPrefillStagesB, kPrefillRowB, 4,
+                                           MODE == kModeGateUp ? kPrefillSyncGateUp : kPrefillSyncDown, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     else
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 16, 8, 1, kDecodeStages, kDecodeRowB, 1, MODE>), dim3(grid),
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, 0, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     return hipGetLastError();
 }
@@ -622,6 +674,7 @@ hipError_t launch_dispatch(const MoeGemmParams& p, const GemmKArgs& a, int max_t
 
 GemmKArgs base_args(const MoeGemmParams& p) {
     GemmKArgs a = {};
+    a.round_counter = p.round_counters;
     a.tiles = p.tiles;
     a.num_tiles = p.num_tiles;
     a.offsets = p.offsets;
@@ -689,6 +742,7 @@ hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
     a.seg_s = p.I;
     a.shared_mtiles = (p.T + bm - 1) / bm;
     a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
+    a.round_counter = p.round_counters + 8;
     return launch_dispatch<kModeDown>(p, a, a.shared_blocks + p.max_routed_tiles * a.ntn_r, stream);
 }
 

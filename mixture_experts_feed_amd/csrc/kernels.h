@@ -22,9 +22,10 @@ int router_ksplit(int T, int H, int NE);
 hipError_t launch_build_masks(const int32_t* topk_idx, const uint8_t* pad, int T, int E, int k, uint64_t* masks,
                               int W, hipStream_t stream);
 // counts / offsets / per-word prefix; optionally the routed tile list for
-// row tiles of `bm` rows (tiles may be NULL).
+// row tiles of `bm` rows (tiles may be NULL) and zeroed GEMM round counters
+// (kRoundCounters ints, or NULL).
 hipError_t launch_scan(const uint64_t* masks, int W, int E, int32_t* prefix, int32_t* counts, int32_t* offsets,
-                       int bm, RoutedTile* tiles, int32_t* num_tiles, hipStream_t stream);
+                       int bm, RoutedTile* tiles, int32_t* num_tiles, int32_t* round_counters, hipStream_t stream);
 hipError_t launch_scatter(const int32_t* topk_idx, const float* topk_w, const uint8_t* pad, const uint64_t* masks,
                           const int32_t* prefix, const int32_t* offsets, int T, int E, int k, int W,
                           int32_t* sorted_slots, int32_t* row_token, float* row_gamma, int32_t* pos,
@@ -54,6 +55,7 @@ struct MoeGemmParams {
     void* y;       // [T*k][H] fp32, slot rows
     void* ysh;     // [T][H] fp32
     void* out;     // [T][H]
+    int32_t* round_counters;   // kRoundCounters ints, zero before gate_up
     int max_routed_tiles;
 };
 int gemm_cfg_for(int dtype, int T, int H, int E, int k, int I);

@@ -38,11 +38,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(const uint64_t* __restrict__
                                                     int32_t* __restrict__ prefix, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets, int bm,
                                                     RoutedTile* __restrict__ tiles,
-                                                    int32_t* __restrict__ num_tiles) {
+                                                    int32_t* __restrict__ num_tiles,
+                                                    int32_t* __restrict__ round_counters) {
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t off[kMaxExperts + 1];
     __shared__ int32_t tstart[kMaxExperts + 1];
     const int lane = lane_id(), wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (round_counters != nullptr && threadIdx.x < kRoundCounters) round_counters[threadIdx.x] = 0;
     for (int e = wv; e < E; e += nw) {
         int carry = 0;
         for (int base = 0; base < W; base += 64) {
@@ -143,9 +145,9 @@ hipError_t launch_build_masks(const int32_t* topk_idx, const uint8_t* pad, int T
 }
 
 hipError_t launch_scan(const uint64_t* masks, int W, int E, int32_t* prefix, int32_t* counts, int32_t* offsets,
-                       int bm, RoutedTile* tiles, int32_t* num_tiles, hipStream_t stream) {
+                       int bm, RoutedTile* tiles, int32_t* num_tiles, int32_t* round_counters, hipStream_t stream) {
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, masks, W, E, prefix, counts, offsets, bm, tiles,
-                       num_tiles);
+                       num_tiles, round_counters);
     return hipGetLastError();
 }
 
