@@ -11,6 +11,8 @@
 // fp64 from the exactly widened fp32 bank and bf16/fp32 hidden states, and
 // sigmoid, selection and softmax run in fp64, so the selected experts are those
 // of exact arithmetic unless two scores differ by less than ~1e-13.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -18,86 +20,132 @@ namespace inkling {
 
 namespace {
 
-constexpr int kTokTile = 64;   // tokens per workgroup (4 waves x 16)
-constexpr int kExpTile = 16;   // logits columns per workgroup
-constexpr int kKChunk = 32;    // hidden-dim chunk staged in LDS
+constexpr int kTokTile = 32;   // tokens per workgroup (2 blocks of 16)
+constexpr int kExpTile = 48;   // logits columns per workgroup (3 blocks of 16)
+constexpr int kKChunk = 64;    // hidden-dim chunk staged in LDS (two buffers)
+constexpr int kRouterThreads = 64 * (kTokTile / 16) * (kExpTile / 16);   // one wave per 16x16 block
 
+// kRowVals consecutive values of a row, kept as raw 16-byte words
+constexpr int kRowVals = 16;
 template <typename TX>
-__device__ __forceinline__ void load8(const TX* p, double* v);
-
-template <>
-__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, double* v) {
-    uint4 q = *reinterpret_cast<const uint4*>(p);
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+struct RowVals {
+    static constexpr int kWords = kRowVals * sizeof(TX) / 16;
+    uint4 q[kWords];
+    __device__ __forceinline__ void load(const TX* p) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = (double)__uint_as_float(w[j] << 16);
-        v[2 * j + 1] = (double)__uint_as_float(w[j] & 0xFFFF0000u);
+        for (int i = 0; i < kWords; ++i) q[i] = reinterpret_cast<const uint4*>(p)[i];
     }
-}
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) q[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __device__ __forceinline__ TX get(int j) const {
+        constexpr int per = 16 / sizeof(TX);   // values per 16-byte word
+        const uint4& w = q[j / per];
+        const int e = j % per;
+        if constexpr (sizeof(TX) == 2) {
+            const uint32_t d = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
+            return (TX)((e & 1) ? (d >> 16) : (d & 0xFFFFu));
+        } else {
+            const uint32_t d = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+            return __uint_as_float(d);
+        }
+    }
+};
 
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, double* v) {
-    float4 a = *reinterpret_cast<const float4*>(p);
-    float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
+// exact widening to fp64
+__device__ __forceinline__ double widen(bf16_t v) { return (double)__uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ double widen(float v) { return (double)v; }
 
 // zpart[ks][t][e] = sum over h in slice ks of x[t][h] * bank[e][h], in fp64.
-// grid (ceil(T/64), ceil(NE/16), ksplit), block 256: wave w owns tokens
-// [16w, 16w+16) of the tile against the tile's 16 bank rows.
+// grid (ceil(T/32), ceil(NE/48), ksplit), 6 waves: wave w owns the 16x16 block
+// (tokens 16*(w%2).., bank rows 16*(w/2)..) of the tile.  Operands are staged
+// in LDS in their own precision and widened to fp64 (exactly) as the MFMA
+// fragments are read; the next chunk's global loads are in flight while the
+// current one is multiplied.
 template <typename TX>
-__global__ __launch_bounds__(256) void router_logits_kernel(const TX* __restrict__ x, const float* __restrict__ bank,
-                                                            double* __restrict__ zpart, int T, int H, int NE,
-                                                            int klen) {
-    __shared__ double xs[kTokTile][kKChunk + 1];
-    __shared__ double gs[kExpTile][kKChunk + 1];
+__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const TX* __restrict__ x,
+                                                                       const float* __restrict__ bank,
+                                                                       double* __restrict__ zpart, int T, int H,
+                                                                       int NE, int klen) {
+    // [buffer][16-row block][k][row in block]: an MFMA operand fragment (lane l
+    // holds row l%16 at k = l/16) is one contiguous run of 64 elements
+    __shared__ TX xs[2][kTokTile / 16][kKChunk][16];
+    __shared__ float gs[2][kExpTile / 16][kKChunk][16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int t0 = blockIdx.x * kTokTile, e0 = blockIdx.y * kExpTile, ks = blockIdx.z;
     const int kbeg = ks * klen;
-    const int kend = min(H, kbeg + klen);
-    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
-    const int xr = tid >> 2, xc = (tid & 3) * 8;
-    const int gr = tid >> 4, gc = (tid & 15) * 2;
-    for (int k0 = kbeg; k0 < kend; k0 += kKChunk) {
-        double v[8];
-        const int t = t0 + xr;
-        if (t < T) {
-            load8<TX>(x + (size_t)t * H + k0 + xc, v);
-        } else {
+    const int nchunks = min(klen, H - kbeg) / kKChunk;
+    const int tb = wv & 1, eb = wv >> 1;   // this wave's token / bank-row block
+    // kChains accumulators (k-steps taken round-robin) so consecutive MFMAs of a
+    // wave are independent
+    constexpr int kChains = 4;
+    f64x4_t acc[kChains];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = 0.0;
+    for (int i = 0; i < kChains; ++i) acc[i] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    // staging: threads [0, 128) load kRowVals hidden values of one token row,
+    // threads [128, 320) kRowVals bank values of one bank row
+    constexpr int kPerRow = kKChunk / kRowVals;   // threads per row
+    constexpr int kXThreads = kTokTile * kPerRow, kGThreads = kExpTile * kPerRow;
+    static_assert(kXThreads + kGThreads <= kRouterThreads, "staging threads");
+    const bool ld_x = tid < kXThreads, ld_g = tid >= kXThreads && tid < kXThreads + kGThreads;
+    const int li = ld_x ? tid : tid - kXThreads;
+    const int lr = li / kPerRow, lc = (li % kPerRow) * kRowVals;
+    const int t = t0 + lr, e = e0 + lr;
+    // two register sets: chunk c+2 is loaded while chunk c is multiplied
+    RowVals<TX> vx0, vx1;
+    RowVals<float> vg0, vg1;
+    auto gload = [&](RowVals<TX>& vx, RowVals<float>& vg, int c) __attribute__((always_inline)) {
+        if (c >= nchunks) return;
+        const int k0 = kbeg + c * kKChunk;
+        if (ld_x) {
+            if (t < T) vx.load(x + (size_t)t * H + k0 + lc);
+            else vx.zero();
+        } else if (ld_g) {
+            if (e < NE) vg.load(bank + (size_t)e * H + k0 + lc);
+            else vg.zero();
         }
+    };
+    auto step = [&](RowVals<TX>& vx, RowVals<float>& vg, int c, auto B_) __attribute__((always_inline)) {
+        constexpr int buf = decltype(B_)::value;
+        if (ld_x) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xs[xr][xc + j] = v[j];
-        const int e = e0 + gr;
-        if (e < NE) {
-            float2 g = *reinterpret_cast<const float2*>(bank + (size_t)e * H + k0 + gc);
-            gs[gr][gc] = (double)g.x;
-            gs[gr][gc + 1] = (double)g.y;
-        } else {
-            gs[gr][gc] = 0.0;
-            gs[gr][gc + 1] = 0.0;
+            for (int j = 0; j < kRowVals; ++j) xs[buf][lr >> 4][lc + j][lr & 15] = vx.get(j);
+        } else if (ld_g) {
+#pragma unroll
+            for (int j = 0; j < kRowVals; ++j) gs[buf][lr >> 4][lc + j][lr & 15] = vg.get(j);
         }
+        // one barrier per chunk: buffer buf was last read two chunks ago, and
+        // every wave has passed the previous chunk's barrier since
         __syncthreads();
+        gload(vx, vg, c + 2);
 #pragma unroll
-        for (int kk = 0; kk < kKChunk; kk += 4) {
+        for (int kk = 0; kk < kKChunk; kk += 4 * kChains) {
             // A (16 tokens x 4): lane holds A[lane%16][lane/16]; B (4 x 16 bank rows): B[lane/16][lane%16]
-            const double a = xs[wv * 16 + (lane & 15)][kk + (lane >> 4)];
-            const double b = gs[lane & 15][kk + (lane >> 4)];
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+            double a[kChains], b[kChains];
+#pragma unroll
+            for (int i = 0; i < kChains; ++i) {
+                a[i] = widen(xs[buf][tb][kk + 4 * i + (lane >> 4)][lane & 15]);
+                b[i] = widen(gs[buf][eb][kk + 4 * i + (lane >> 4)][lane & 15]);
+            }
+#pragma unroll
+            for (int i = 0; i < kChains; ++i) acc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[i], acc[i], 0, 0, 0);
         }
-        __syncthreads();
+    };
+    gload(vx0, vg0, 0);
+    gload(vx1, vg1, 1);
+    for (int c = 0; c < nchunks; c += 2) {
+        step(vx0, vg0, c, std::integral_constant<int, 0>{});
+        if (c + 1 < nchunks) step(vx1, vg1, c + 1, std::integral_constant<int, 1>{});
     }
     // fp64 16x16x4 result layout: lane holds D[i][j] for rows i = lane/16 + 4*r
     // (r = 0..3) and column j = lane % 16 (unlike the fp32 16x16 layouts, whose
     // rows are 4*(lane/16) + r).
-    const int e = e0 + (lane & 15);
+    const int eo = e0 + eb * 16 + (lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int t = t0 + wv * 16 + (lane >> 4) + 4 * r;
-        if (t < T && e < NE) zpart[((size_t)ks * T + t) * NE + e] = acc[r];
+        const int to = t0 + tb * 16 + (lane >> 4) + 4 * r;
+        if (to < T && eo < NE) zpart[((size_t)ks * T + to) * NE + eo] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
     }
 }
 
@@ -192,8 +240,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double* __rest
 int router_ksplit(int T, int H, int NE) {
     const int tiles = ((T + kTokTile - 1) / kTokTile) * ((NE + kExpTile - 1) / kExpTile);
     int ks = 1;
-    // split the hidden dim until ~512 workgroups exist, keeping >= 256 per slice
-    while (tiles * ks * 2 <= 512 && (H / (ks * 2)) >= 256 && (H % (ks * 2 * kKChunk)) == 0) ks *= 2;
+    // split the hidden dim until ~3 workgroups per CU exist (768), keeping >= 256 per slice
+    while (tiles * ks * 2 <= 768 && (H / (ks * 2)) >= 256 && (H % (ks * 2 * kKChunk)) == 0) ks *= 2;
     return ks;
 }
 
@@ -202,11 +250,11 @@ hipError_t launch_router_logits(int dtype, const void* x, const float* bank, dou
     dim3 grid((T + kTokTile - 1) / kTokTile, (NE + kExpTile - 1) / kExpTile, ksplit);
     const int klen = H / ksplit;
     if (dtype == 1)
-        hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(256), 0, stream, (const bf16_t*)x, bank, zpart,
-                           T, H, NE, klen);
+        hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(kRouterThreads), 0, stream, (const bf16_t*)x, bank,
+                           zpart, T, H, NE, klen);
     else
-        hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, stream, (const float*)x, bank, zpart, T,
-                           H, NE, klen);
+        hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(kRouterThreads), 0, stream, (const float*)x, bank,
+                           zpart, T, H, NE, klen);
     return hipGetLastError();
 }
 
