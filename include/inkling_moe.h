@@ -149,9 +149,9 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
  *   1 router logits, 2 router selection, 3 permutation (masks, scan, scatter),
  *   4 gate_up grouped GEMM + SwiGLU (routed and shared),
  *   5 down grouped GEMM (routed and shared), 6 combine.
- * events[] holds INKLING_STAGE_EVENTS hipEvent_t handles created by the caller;
- * the array must stay valid until the hook is cleared with NULL.  Adds no
- * synchronisation.  Returns INKLING_ERR_INVALID_ARGUMENT if n_events is too
+ * events[] holds INKLING_STAGE_EVENTS hipEvent_t handles created by the caller
+ * (a NULL entry skips that boundary); the array must stay valid until the hook
+ * is cleared with NULL.  Adds no synchronisation.  Returns INKLING_ERR_INVALID_ARGUMENT if n_events is too
  * small. */
 #define INKLING_STAGE_EVENTS 7
 int inkling_moe_set_stage_events(void* const* events, int n_events);

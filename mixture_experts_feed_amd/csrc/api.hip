@@ -14,7 +14,7 @@ thread_local int g_last_hip_error = 0;
 thread_local void* const* g_stage_events = nullptr;
 
 inline hipError_t mark(int i, hipStream_t s) {
-    if (g_stage_events == nullptr) return hipSuccess;
+    if (g_stage_events == nullptr || g_stage_events[i] == nullptr) return hipSuccess;
     return hipEventRecord((hipEvent_t)g_stage_events[i], s);
 }
 

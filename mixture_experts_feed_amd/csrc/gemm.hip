@@ -214,12 +214,12 @@ template <typename TE, int BN, int BM, int WN, int WM, int SA, int SB, int ROWB,
 __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs a) {
     constexpr int NW = WN * WM;                     // waves per workgroup
     static_assert(NW == 8, "eight waves: two per SIMD");
-    static_assert(SB >= 2 && SA <= 4 && (SA == SB || SA == SB + 1), "weight stages = token stages (+1)");
+    static_assert(SB >= 2 && SA <= 8 && (SA == SB || SA == SB + 1), "weight stages = token stages (+1)");
     // stages unrolled per K-loop iteration: every weight and token buffer index
     // repeats, and the fragment double buffers keep a compile-time parity
     constexpr int U = SA == SB ? SA : SA * SB;
     static_assert(U % 2 == 0, "even unroll");
-    static_assert(ROWB == 64 || ROWB == 128, "64 or 128 bytes of K per row and stage");
+    static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "64, 128 or 256 bytes of K per row and stage");
     constexpr int CH = ROWB / 16;                   // 16-byte chunks per row and stage
     constexpr int KS = ROWB / 64;                   // MFMA k-steps per stage (64 bytes of K each)
     constexpr int EPC = 16 / sizeof(TE);            // elements per 16-byte chunk
@@ -240,23 +240,39 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     __shared__ __attribute__((aligned(16))) uint8_t sa1[A_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t sa2[SA > 2 ? A_BYTES : SMALL];
     __shared__ __attribute__((aligned(16))) uint8_t sa3[SA > 3 ? A_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sa4[SA > 4 ? A_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sa5[SA > 5 ? A_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sa6[SA > 6 ? A_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sa7[SA > 7 ? A_BYTES : SMALL];
     __shared__ __attribute__((aligned(16))) uint8_t sb0[B_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t sb1[B_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t sb2[SB > 2 ? B_BYTES : SMALL];
     __shared__ __attribute__((aligned(16))) uint8_t sb3[SB > 3 ? B_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sb4[SB > 4 ? B_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sb5[SB > 5 ? B_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sb6[SB > 6 ? B_BYTES : SMALL];
+    __shared__ __attribute__((aligned(16))) uint8_t sb7[SB > 7 ? B_BYTES : SMALL];
     auto stage_a = [&](auto S_) -> uint8_t* {
         constexpr int i = decltype(S_)::value % SA;
         if constexpr (i == 0) return sa0;
         else if constexpr (i == 1) return sa1;
         else if constexpr (i == 2) return sa2;
-        else return sa3;
+        else if constexpr (i == 3) return sa3;
+        else if constexpr (i == 4) return sa4;
+        else if constexpr (i == 5) return sa5;
+        else if constexpr (i == 6) return sa6;
+        else return sa7;
     };
     auto stage_b = [&](auto S_) -> uint8_t* {
         constexpr int i = decltype(S_)::value % SB;
         if constexpr (i == 0) return sb0;
         else if constexpr (i == 1) return sb1;
         else if constexpr (i == 2) return sb2;
-        else return sb3;
+        else if constexpr (i == 3) return sb3;
+        else if constexpr (i == 4) return sb4;
+        else if constexpr (i == 5) return sb5;
+        else if constexpr (i == 6) return sb6;
+        else return sb7;
     };
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -289,7 +305,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     // LDS rows are ROWB bytes; the 16-byte chunk c of row r sits at chunk
     // position c ^ sw(r), which makes the fragment reads below conflict-free.
     // A wave load fills RPL rows: lane -> row lane / CH, chunk position lane % CH.
-    auto sw = [](int r) { return CH == 4 ? ((r >> 1) & 3) : (r & 7); };
+    auto sw = [](int r) { return CH == 4 ? ((r >> 1) & 3) : CH == 8 ? (r & 7) : (r & 15); };
     const int lr = lane / CH, lp = lane % CH;
     const TE* a_src[A_PW];
     const TE* b_src[B_PW];
@@ -631,11 +647,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 //       128 tokens (token blocks interleaved), 2 stages of 128-byte rows.
 // cfg 1 (few rows per expert, decode): 256 weight rows x 16 tokens, 8 waves
 //       along the weight rows, 4 stages.
-constexpr int kBN = 256;
 constexpr int kPrefillStagesA = 2, kPrefillStagesB = 2, kPrefillRowB = 128;
 // tile-round rendezvous per XCD: pays off for the long-K gate_up tiles only
 constexpr int kPrefillSyncGateUp = 1, kPrefillSyncDown = 0;
-constexpr int kDecodeStages = 4, kDecodeRowB = 128;
+constexpr int kPrefillBN = 256;
+constexpr int kDecodeBN = 128, kDecodeStages = 4, kDecodeRowB = 128, kDecodeGridPerCU = 1;
+int cfg_bn(int cfg) { return cfg == 0 ? kPrefillBN : kDecodeBN; }
 
 int num_cus() {
     static int n = 0;
@@ -654,14 +671,14 @@ template <typename TE, int MODE>
 hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t stream) {
     if (max_tiles <= 0) return hipSuccess;
     // persistent: at most one workgroup per CU (LDS), a multiple of the 8 XCDs
-    int grid = std::min(max_tiles, num_cus());
+    int grid = std::min(max_tiles, num_cus() * (cfg == 0 ? 1 : kDecodeGridPerCU));
     grid = (grid + 7) / 8 * 8;
     if (cfg == 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 256, 4, 2, kPrefillStagesA, kPrefillStagesB, kPrefillRowB, 4,
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB, kPrefillRowB, 4,
                                            MODE == kModeGateUp ? kPrefillSyncGateUp : kPrefillSyncDown, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     else
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, 256, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, 0, MODE>), dim3(grid),
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, kDecodeBN, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, 0, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     return hipGetLastError();
 }
@@ -708,14 +725,14 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     a.out_routed = p.act_r;
     a.K_r = p.H;
     a.N_r = 2 * p.I;
-    a.ntn_r = (a.N_r + kBN - 1) / kBN;
+    a.ntn_r = (a.N_r + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
     a.has_routed = 1;
     a.A_shared = p.wsh_gu;
     a.B_shared = p.x;
     a.out_shared = p.act_sh;
     a.K_s = p.H;
     a.N_s = 2 * p.I * p.S;
-    a.ntn_s = (a.N_s + kBN - 1) / kBN;
+    a.ntn_s = (a.N_s + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
     a.seg_s = p.H;
     a.shared_mtiles = (p.T + bm - 1) / bm;
     a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
@@ -730,7 +747,7 @@ hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
     a.out_routed = p.y;
     a.K_r = p.I;
     a.N_r = p.H;
-    a.ntn_r = (p.H + kBN - 1) / kBN;
+    a.ntn_r = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
     a.has_routed = 1;
     // shared experts: act_sh [T][S*I] against the S down projections concatenated along K
     a.A_shared = p.wsh_d;

@@ -169,17 +169,35 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double* __rest
     const int NE = E + S;
     double sc[kMaxPerLane];
     bool live[kMaxPerLane];
+    // logits: sum of the hidden-dim slices in slice order; the loads of four
+    // slices for all of the lane's experts are issued together
+    double z[kMaxPerLane];
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) z[j] = 0.0;
+    for (int s0 = 0; s0 < ksplit; s0 += 4) {
+        double p[4][kMaxPerLane];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < kMaxPerLane; ++j) {
+                const int e = lane + 64 * j;
+                p[u][j] = (s0 + u < ksplit && e < NE) ? zpart[((size_t)(s0 + u) * T + t) * NE + e] : 0.0;
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < kMaxPerLane; ++j)
+                if (s0 + u < ksplit) z[j] += p[u][j];
+    }
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         const int e = lane + 64 * j;
         live[j] = false;
         sc[j] = 0.0;
         if (e < NE) {
-            double z = 0.0;
-            for (int s = 0; s < ksplit; ++s) z += zpart[((size_t)s * T + t) * NE + e];
-            zs[wv][e] = z;
+            zs[wv][e] = z[j];
             if (e < E) {
-                sc[j] = 1.0 / (1.0 + exp(-z)) + (double)bias[e];
+                sc[j] = 1.0 / (1.0 + exp(-z[j])) + (double)bias[e];
                 live[j] = true;
             }
         }
