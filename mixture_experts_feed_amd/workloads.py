@@ -101,6 +101,13 @@ WORKLOADS: Dict[str, Workload] = {
         "decode_h6144", T=32, hidden=6144, n_routed=128, top_k=8, n_shared=2, intermediate=2048,
         dtype="bf16", route_scale=2.5, global_scale=1.0,
         gate_dist=("uniform", 0.05), bias_dist=("uniform", 0.05), family_seed=0, x_seed=0),
+    # Inkling's own MoE defaults (InklingTextConfig on the configuration page:
+    # hidden 6144, 256 routed experts, 6 per token, 2 shared, moe intermediate
+    # 3072, route_scale 8), at the prefill token count and value distributions
+    "inkling_default_h6144": Workload(
+        "inkling_default_h6144", T=8192, hidden=6144, n_routed=256, top_k=6, n_shared=2, intermediate=3072,
+        dtype="bf16", route_scale=8.0, global_scale=1.0,
+        gate_dist=("uniform", 0.05), bias_dist=("uniform", 0.05), family_seed=0, x_seed=0),
     "skewed_h6144": Workload(
         "skewed_h6144", T=16384, hidden=6144, n_routed=128, top_k=8, n_shared=2, intermediate=2048,
         dtype="bf16", route_scale=2.5, global_scale=1.0,

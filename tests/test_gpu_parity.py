@@ -186,3 +186,16 @@ def test_prefill_h6144(h6144_experts):
 
 def test_skewed_h6144(h6144_experts):
     _sampled_parity("skewed_h6144", h6144_experts)
+
+
+def test_inkling_default_h6144():
+    """Inkling's own MoE shape (configuration page defaults: 256 routed experts,
+    top-6, 2 shared, intermediate 3072, route_scale 8) at full width."""
+    w = wl.WORKLOADS["inkling_default_h6144"]
+    _say("[parity] drawing the Inkling-default expert weights on the device (~29 GB)")
+    experts = wl.expert_weights(w, device=DEV)
+    try:
+        _sampled_parity("inkling_default_h6144", experts, n_sample=16)
+    finally:
+        del experts
+        torch.cuda.empty_cache()

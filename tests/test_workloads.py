@@ -56,3 +56,13 @@ def test_skewed_bias_leaves_a_fifth_of_experts_empty():
     # outlier rows: about 10% of rows have std 4
     rs = np.std(x, axis=1)
     assert 0.08 < float(np.mean(rs > 2.0)) < 0.12
+
+
+def test_inkling_default_shape_matches_configuration_page():
+    """InklingTextConfig defaults (configuration page): hidden_size 6144,
+    n_routed_experts 256, num_experts_per_tok 6, n_shared_experts 2,
+    moe_intermediate_size 3072, route_scale 8.0; init std 0.02 (layers page)."""
+    w = wl.WORKLOADS["inkling_default_h6144"]
+    assert (w.hidden, w.n_routed, w.top_k, w.n_shared, w.intermediate) == (6144, 256, 6, 2, 3072)
+    assert w.route_scale == 8.0 and w.global_scale == 1.0 and w.w_std == 0.02
+    assert w.dtype == "bf16"
