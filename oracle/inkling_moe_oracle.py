@@ -19,6 +19,8 @@ What it computes follows the Inkling layers page
     shared gammas before summation.
   * InklingMoE.forward: routed + shared outputs summed, output shaped like the
     input; padded tokens are excluded from routed dispatch.
+  * InklingDenseMLP: the dense SwiGLU MLP on the same interleaved layout,
+    scaled by its global_scale parameter.
 
 Everything runs in float64 on the exact input values (bf16 and fp32 inputs widen
 to fp64 without error, and their pairwise products are exact in fp64), with
@@ -30,14 +32,16 @@ where the pages are silent:
   * SwiGLU is silu(gate) * up with no clamp (hidden_act 'silu' on the
     configuration page, InklingTextConfig);
   * no normalisation of the hidden states inside the gate;
-  * padded tokens still pass through the shared experts.
+  * padded tokens still pass through the shared experts;
+  * InklingDenseMLP's global_scale scales the MLP output.
 
 Pins (tests/test_oracle_pins.py, all CPU): brute-force top-k over every subset
 on tiny inputs, forced exact ties, the closed form sigma/sum(sigma) of the
 log-sigmoid softmax, gammas summing to route_scale*global_scale, the
 interleaved SwiGLU against the de-interleaved textbook form, a one-expert top-1
-MoE against a dense SwiGLU MLP, token independence, expert relabelling, and a
-hand-derived worked example (test_hand_derived_example).  Agreement with
+MoE against a dense SwiGLU MLP, token independence, expert relabelling, a
+hand-derived worked example (test_hand_derived_example), and the dense MLP
+against the textbook SwiGLU and against a one-expert top-1 MoE.  Agreement with
 the HuggingFace InklingTopkRouter or a real checkpoint: parity unpinned (neither
 exists here).
 """
@@ -242,3 +246,16 @@ def moe_forward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int,
     if len(wsh_gu):
         out += shared_experts(xr, wsh_gu, wsh_d, sg[rows])
     return out, routing
+
+
+# --------------------------------------------------------------------------
+# InklingDenseMLP (layers page, InklingDenseMLP)
+# --------------------------------------------------------------------------
+
+def dense_mlp(x, w_gu, w_d, global_scale: float) -> np.ndarray:
+    """InklingDenseMLP.forward: the dense MLP over the fused interleaved
+    gate_up projection [2I, H] (row 2j gate_j, 2j+1 up_j), down projection
+    [H, I], and the module's global_scale parameter.  The page does not say
+    where global_scale enters; it is read as scaling the MLP output (equal in
+    exact arithmetic to scaling the activation, since down_proj is linear)."""
+    return float(global_scale) * expert_ffn(x, w_gu, w_d)

@@ -343,3 +343,35 @@ def test_hand_derived_example():
     y1 = (9 / 7) * 2 * silu(1) * np.array([1.0, 1.0])
     ysh = (6 / 7) * silu(1) * np.array([2.0, 1.0])
     assert np.allclose(out2[0], y0 + y1 + ysh, rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------- dense MLP
+
+def test_dense_mlp_is_textbook_swiglu_times_scale():
+    rng = np.random.default_rng(21)
+    T, H, I = 9, 12, 5
+    x = rng.standard_normal((T, H))
+    w_gu = rng.standard_normal((2 * I, H)) * 0.3
+    w_d = rng.standard_normal((H, I)) * 0.3
+    g, u = x @ w_gu[0::2].T, x @ w_gu[1::2].T
+    textbook = ((g / (1.0 + np.exp(-g))) * u) @ w_d.T
+    out = oracle.dense_mlp(x, w_gu, w_d, 0.75)
+    assert np.allclose(out, 0.75 * textbook, rtol=1e-13, atol=1e-14)
+    # linear in global_scale; zero scale gives zero
+    assert np.allclose(oracle.dense_mlp(x, w_gu, w_d, 1.5), 2.0 * out, rtol=1e-14, atol=0)
+    assert np.all(oracle.dense_mlp(x, w_gu, w_d, 0.0) == 0.0)
+
+
+def test_dense_mlp_equals_one_expert_moe_with_route_scale_as_global_scale():
+    """A top-1 MoE over a single expert with no shared experts gives that expert
+    gamma = route_scale * global_scale (softmax over one logit is 1), so it is
+    the dense MLP with that scale, whatever the gate bank and bias."""
+    rng = np.random.default_rng(22)
+    T, H, I = 7, 10, 6
+    x = rng.standard_normal((T, H))
+    w_gu = rng.standard_normal((1, 2 * I, H)) * 0.3
+    w_d = rng.standard_normal((1, H, I)) * 0.3
+    bank = rng.standard_normal((1, H))
+    bias = rng.standard_normal(1)
+    moe, _ = oracle.moe_forward(x, bank, bias, w_gu, w_d, [], [], 1, 2.0, 0.625)
+    assert np.allclose(moe, oracle.dense_mlp(x, w_gu[0], w_d[0], 1.25), rtol=1e-12, atol=1e-13)
