@@ -187,6 +187,7 @@ def main():
     ap.add_argument("--workload", default="prefill_h6144")
     ap.add_argument("--decode-workload", default="decode_h6144")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the InklingDenseMLP line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -298,6 +299,25 @@ def main():
                             "bytes_alg": bytes_alg, "n_touched_experts": n_touched,
                             "stage_ms": {n: round(dstage[i], 4) for i, n in enumerate(B.STAGES)}}
         log(f"[bench] decode {dms:.3f} ms, {result['decode']['hbm_GBps']} GB/s")
+
+    if not args.no_dense:
+        # InklingDenseMLP of the first layer (intermediate 24576) on the same token count
+        dw = wl.DENSE_WORKLOADS["dense_h6144"]
+        dn = wl.dense_inputs(dw, device=dev)
+        ddims = B.make_dense_dims(dw.T, dw.hidden, dw.intermediate, dw.torch_dtype)
+        dws = torch.empty(max(1, B.dense_workspace_size(ddims)), dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(dn["x"])
+
+        def dense_call():
+            B.dense_mlp_forward(dn["x"], dn["gate_up"], dn["down"], dw.global_scale, out=dout, workspace=dws)
+
+        dms, _ = run_timed(torch, B, dense_call, args.steps, args.warmup, events)
+        dtf = dw.flops_alg() / (dms * 1e-3) / 1e12
+        result["dense_mlp"] = {"workload": dw.name, "T": dw.T, "hidden": dw.hidden, "intermediate": dw.intermediate,
+                               "ms_per_step": round(dms, 4), "TFLOP_s": round(dtf, 2),
+                               "frac_of_peak": round(dtf / PEAK_BF16_TFLOPS, 4), "flops_per_step": dw.flops_alg()}
+        log(f"[bench] dense MLP {dms:.3f} ms, {dtf:.1f} TFLOP/s")
+        del dn, dws, dout
 
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_tokens} tokens")

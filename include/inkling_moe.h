@@ -143,6 +143,33 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
                         inkling_route_out_t* route_out, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * InklingDenseMLP (layers page): the dense SwiGLU MLP on the fused interleaved
+ * gate_up layout, scaled by the module's global_scale:
+ *   out = global_scale * down . (silu(gate) * up),  [gate, up] = gate_up . x
+ * (reading: the page does not say where global_scale enters; it scales the
+ * output, applied here to the activation, which is the same in exact
+ * arithmetic).  intermediate is the dense intermediate size (InklingTextConfig
+ * dense_intermediate_size, defaulting to intermediate_size = 24576).
+ *   x        [T][hidden] (dtype);  gate_up [2*intermediate][hidden], row 2j =
+ *   gate_j, 2j+1 = up_j;  down [hidden][intermediate];  out [T][hidden]
+ *   (out_dtype; INKLING_F32 keeps the fp32 result unrounded), must not alias x.
+ * Same conventions and errors as inkling_moe_forward; limits hidden % 64 == 0,
+ * intermediate % 64 == 0.
+ */
+typedef struct {
+    int64_t T;
+    int32_t hidden;
+    int32_t intermediate;
+    int32_t dtype;      /* inkling_dtype_t of x and the weights */
+    int32_t out_dtype;  /* inkling_dtype_t of out */
+} inkling_dense_dims_t;
+
+int inkling_dense_mlp_workspace_size(const inkling_dense_dims_t* dims, size_t* bytes);
+
+int inkling_dense_mlp_forward(const inkling_dense_dims_t* dims, const void* x, const void* gate_up, const void* down,
+                              float global_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage timing (instrumentation for benchmarks).  When `events` is non-NULL,
  * each later inkling_moe_forward on the calling thread records, on its stream,
  * events[0] before the first launch and events[i] after stage i:

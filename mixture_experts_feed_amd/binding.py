@@ -24,7 +24,8 @@ INKLING_F32 = 0
 INKLING_BF16 = 1
 
 EXPORTED = ("inkling_moe_workspace_size", "inkling_moe_route", "inkling_moe_forward",
-            "inkling_moe_strerror", "inkling_moe_last_hip_error", "inkling_moe_set_stage_events")
+            "inkling_moe_strerror", "inkling_moe_last_hip_error", "inkling_moe_set_stage_events",
+            "inkling_dense_mlp_workspace_size", "inkling_dense_mlp_forward")
 INKLING_STAGE_EVENTS = 7
 STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "combine")
 
@@ -32,6 +33,11 @@ STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "c
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("hidden", ctypes.c_int32), ("n_routed", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class DenseDims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
@@ -87,6 +93,12 @@ def load() -> ctypes.CDLL:
     lib.inkling_moe_last_hip_error.restype = ctypes.c_int
     lib.inkling_moe_set_stage_events.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.inkling_moe_set_stage_events.restype = ctypes.c_int
+    lib.inkling_dense_mlp_workspace_size.argtypes = [ctypes.POINTER(DenseDims), ctypes.POINTER(ctypes.c_size_t)]
+    lib.inkling_dense_mlp_workspace_size.restype = ctypes.c_int
+    lib.inkling_dense_mlp_forward.argtypes = [ctypes.POINTER(DenseDims), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p]
+    lib.inkling_dense_mlp_forward.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -232,3 +244,46 @@ def set_stage_events(events: Optional[ctypes.Array]) -> None:
     rc = load().inkling_moe_set_stage_events(None if events is None else ctypes.cast(events, ctypes.c_void_p), n)
     if rc != INKLING_OK:
         raise InklingError(rc, "inkling_moe_set_stage_events")
+
+
+def make_dense_dims(T, hidden, intermediate, dtype, out_dtype=None) -> DenseDims:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    ocode = code if out_dtype is None else (out_dtype if isinstance(out_dtype, int) else _dtype_code(out_dtype))
+    return DenseDims(int(T), int(hidden), int(intermediate), code, ocode)
+
+
+def dense_workspace_size(dims: DenseDims) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().inkling_dense_mlp_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    if rc != INKLING_OK:
+        raise InklingError(rc, "inkling_dense_mlp_workspace_size")
+    return int(n.value)
+
+
+def dense_mlp_forward(x: torch.Tensor, gate_up: torch.Tensor, down: torch.Tensor, global_scale: float,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """inkling_dense_mlp_forward: InklingDenseMLP on x [T, H] with gate_up
+    [2I, H] (interleaved) and down [H, I]."""
+    T, H = x.shape
+    twoI = gate_up.shape[0]
+    for t, n in ((x, "x"), (gate_up, "gate_up"), (down, "down")):
+        _need(t, n, x.dtype)
+    if gate_up.shape != (twoI, H) or down.shape != (H, twoI // 2):
+        raise ValueError("gate_up must be [2I, H] and down [H, I]")
+    if out is not None:
+        out_dtype = out.dtype
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    dims = make_dense_dims(T, H, twoI // 2, x.dtype, out_dtype)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(1, dense_workspace_size(dims)), dtype=torch.uint8, device=dev)
+    rc = load().inkling_dense_mlp_forward(ctypes.byref(dims), x.data_ptr(), gate_up.data_ptr(), down.data_ptr(),
+                                          float(global_scale), out.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream(dev))
+    if rc != INKLING_OK:
+        raise InklingError(rc, "inkling_dense_mlp_forward")
+    return out

@@ -143,6 +143,38 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
 
 }  // namespace
 
+// ---- InklingDenseMLP ------------------------------------------------------
+int check_dense_dims(const inkling_dense_dims_t* d) {
+    if (d == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    if (d->T < 0 || d->hidden <= 0 || d->intermediate <= 0) return INKLING_ERR_INVALID_ARGUMENT;
+    if (d->dtype != INKLING_F32 && d->dtype != INKLING_BF16) return INKLING_ERR_UNSUPPORTED;
+    if (d->out_dtype != INKLING_F32 && d->out_dtype != INKLING_BF16) return INKLING_ERR_UNSUPPORTED;
+    if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return INKLING_ERR_UNSUPPORTED;
+    if (d->T > INT32_MAX) return INKLING_ERR_UNSUPPORTED;
+    return INKLING_OK;
+}
+
+struct DenseLayout {
+    size_t gamma, round_counters, act, ysh, total;
+};
+
+DenseLayout make_dense_layout(const inkling_dense_dims_t* d) {
+    DenseLayout L = {};
+    const size_t T = (size_t)d->T, es = d->dtype == INKLING_BF16 ? 2 : 4;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.gamma = take(T * 4);
+    L.round_counters = take(kRoundCounters * 4);
+    L.act = take(T * (size_t)d->intermediate * es);
+    L.ysh = take(T * (size_t)d->hidden * 4);
+    L.total = o;
+    return L;
+}
+
 extern "C" {
 
 int inkling_moe_workspace_size(const inkling_moe_dims_t* dims, size_t* bytes) {
@@ -237,12 +269,59 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
     p.out = out;
     p.max_routed_tiles = L.max_tiles;
     p.round_counters = at<int32_t>(workspace, L.round_counters);
+    p.has_routed = 1;
     HIP_TRY(launch_gate_up(p, s));
     HIP_TRY(mark(4, s));
     HIP_TRY(launch_down(p, s));
     HIP_TRY(mark(5, s));
     HIP_TRY(launch_combine(p, s));
     HIP_TRY(mark(6, s));
+    return INKLING_OK;
+}
+
+int inkling_dense_mlp_workspace_size(const inkling_dense_dims_t* dims, size_t* bytes) {
+    const int rc = check_dense_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (bytes == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    *bytes = make_dense_layout(dims).total;
+    return INKLING_OK;
+}
+
+int inkling_dense_mlp_forward(const inkling_dense_dims_t* dims, const void* x, const void* gate_up, const void* down,
+                              float global_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    const int rc = check_dense_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (dims->T == 0) return INKLING_OK;
+    if (x == nullptr || gate_up == nullptr || down == nullptr || out == nullptr || out == x)
+        return INKLING_ERR_INVALID_ARGUMENT;
+    const DenseLayout L = make_dense_layout(dims);
+    if (workspace == nullptr || workspace_bytes < L.total) return INKLING_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const int T = (int)dims->T, H = dims->hidden, I = dims->intermediate;
+    // one always-on expert over every token, its gamma = global_scale
+    MoeGemmParams p = {};
+    p.dtype = dims->dtype == INKLING_BF16 ? 1 : 0;
+    p.out_dtype = dims->out_dtype == INKLING_BF16 ? 1 : 0;
+    p.cfg = gemm_cfg_for(p.dtype, T, H, 1, 1, I);
+    p.T = T;
+    p.H = H;
+    p.E = 0;
+    p.S = 1;
+    p.I = I;
+    p.k = 0;
+    p.x = x;
+    p.wsh_gu = gate_up;
+    p.wsh_d = down;
+    p.shared_g = at<float>(workspace, L.gamma);
+    p.act_sh = at<void>(workspace, L.act);
+    p.ysh = at<void>(workspace, L.ysh);
+    p.out = out;
+    p.round_counters = at<int32_t>(workspace, L.round_counters);
+    p.has_routed = 0;
+    HIP_TRY(launch_dense_prep(at<float>(workspace, L.gamma), T, global_scale, p.round_counters, s));
+    HIP_TRY(launch_gate_up(p, s));
+    HIP_TRY(launch_down(p, s));
+    HIP_TRY(launch_combine(p, s));
     return INKLING_OK;
 }
 

@@ -641,6 +641,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
 }
 
+__global__ __launch_bounds__(256) void dense_prep_kernel(float* __restrict__ gamma, int T, float value,
+                                                         int32_t* __restrict__ round_counters) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < T) gamma[i] = value;
+    if (blockIdx.x == 0 && threadIdx.x < kRoundCounters) round_counters[threadIdx.x] = 0;
+}
+
 // ---- tile configurations ---------------------------------------------------
 // cfg 0 (many rows per expert): 256 weight rows x 256 tokens, 8 waves (two per
 //       SIMD) as 4 along the weight rows x 2 along the tokens, each 64 rows x
@@ -726,7 +733,7 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     a.K_r = p.H;
     a.N_r = 2 * p.I;
     a.ntn_r = (a.N_r + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
-    a.has_routed = 1;
+    a.has_routed = p.has_routed;
     a.A_shared = p.wsh_gu;
     a.B_shared = p.x;
     a.out_shared = p.act_sh;
@@ -736,7 +743,8 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     a.seg_s = p.H;
     a.shared_mtiles = (p.T + bm - 1) / bm;
     a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
-    return launch_dispatch<kModeGateUp>(p, a, a.shared_blocks + p.max_routed_tiles * a.ntn_r, stream);
+    return launch_dispatch<kModeGateUp>(p, a, a.shared_blocks + (p.has_routed ? p.max_routed_tiles * a.ntn_r : 0),
+                                        stream);
 }
 
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
@@ -748,7 +756,7 @@ hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
     a.K_r = p.I;
     a.N_r = p.H;
     a.ntn_r = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
-    a.has_routed = 1;
+    a.has_routed = p.has_routed;
     // shared experts: act_sh [T][S*I] against the S down projections concatenated along K
     a.A_shared = p.wsh_d;
     a.B_shared = p.act_sh;
@@ -760,7 +768,8 @@ hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
     a.shared_mtiles = (p.T + bm - 1) / bm;
     a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
     a.round_counter = p.round_counters + 8;
-    return launch_dispatch<kModeDown>(p, a, a.shared_blocks + p.max_routed_tiles * a.ntn_r, stream);
+    return launch_dispatch<kModeDown>(p, a, a.shared_blocks + (p.has_routed ? p.max_routed_tiles * a.ntn_r : 0),
+                                      stream);
 }
 
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream) {
@@ -774,6 +783,12 @@ hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream) {
     else
         hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
                            reinterpret_cast<float*>(p.out), p.T, p.H, p.k);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_prep(float* gamma, int T, float value, int32_t* round_counters, hipStream_t stream) {
+    const int blocks = std::max(1, (T + 255) / 256);
+    hipLaunchKernelGGL(dense_prep_kernel, dim3(blocks), dim3(256), 0, stream, gamma, T, value, round_counters);
     return hipGetLastError();
 }
 

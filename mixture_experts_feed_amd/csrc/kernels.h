@@ -56,6 +56,7 @@ struct MoeGemmParams {
     void* ysh;     // [T][H] fp32
     void* out;     // [T][H]
     int32_t* round_counters;   // kRoundCounters ints, zero before gate_up
+    int has_routed;            // 0: shared tiles only (dense MLP); tiles / num_tiles unused
     int max_routed_tiles;
 };
 int gemm_cfg_for(int dtype, int T, int H, int E, int k, int I);
@@ -64,5 +65,8 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
 // routed (act_r -> y) and shared (act_sh -> ysh) down projections, one launch
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream);
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream);
+// gamma[t] = value for t < T; the GEMM round counters zeroed (the dense MLP's
+// stand-in for the router and the permutation)
+hipError_t launch_dense_prep(float* gamma, int T, float value, int32_t* round_counters, hipStream_t stream);
 
 }  // namespace inkling

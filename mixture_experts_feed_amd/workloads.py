@@ -204,3 +204,57 @@ def make_inputs(w: Workload, device="cpu", T: Optional[int] = None, with_experts
     if with_experts:
         d["w_gu"], d["w_d"], d["wsh_gu"], d["wsh_d"] = expert_weights(w, device)
     return d
+
+
+# ---- InklingDenseMLP -------------------------------------------------------
+_TID_DENSE_X = 11
+_TID_DENSE_GU = 12
+_TID_DENSE_D = 13
+
+
+@dataclasses.dataclass(frozen=True)
+class DenseWorkload:
+    """InklingDenseMLP inputs: x [T, hidden] ~ N(0,1); gate_up [2I, hidden] and
+    down [hidden, I] ~ N(0, w_std); the module's global_scale."""
+    name: str
+    T: int
+    hidden: int
+    intermediate: int
+    dtype: str = "bf16"
+    global_scale: float = 1.0
+    w_std: float = 0.02
+    seed: int = 0
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def flops_alg(self) -> float:
+        return 6.0 * self.T * self.hidden * self.intermediate
+
+
+DENSE_WORKLOADS: Dict[str, DenseWorkload] = {
+    # the first Inkling layer's dense MLP (dense_mlp_idx 0): intermediate_size
+    # 24576 on the configuration page, at the prefill token count
+    "dense_h6144": DenseWorkload("dense_h6144", T=8192, hidden=6144, intermediate=24576),
+}
+
+
+def dense_custom(name: str = "dense_custom", **kw) -> DenseWorkload:
+    return DenseWorkload(name, **kw)
+
+
+def dense_inputs(w: DenseWorkload, device="cpu") -> Dict[str, torch.Tensor]:
+    """x drawn on the CPU generator; the weights on `device` (as for experts)."""
+    x = torch.empty((w.T, w.hidden), dtype=torch.float32)
+    x.normal_(0.0, 1.0, generator=_gen(_seed_plain(w.seed, _TID_DENSE_X, w.T)))
+    gu = _draw((2 * w.intermediate, w.hidden), ("normal", w.w_std),
+               _gen(_seed_plain(w.seed, _TID_DENSE_GU, 0), device), device)
+    dn = _draw((w.hidden, w.intermediate), ("normal", w.w_std),
+               _gen(_seed_plain(w.seed, _TID_DENSE_D, 0), device), device)
+    return {"x": x.to(w.torch_dtype).to(device), "gate_up": gu.to(w.torch_dtype), "down": dn.to(w.torch_dtype),
+            "global_scale": w.global_scale}
+
+
+def _seed_plain(base: int, tensor_id: int, sub: int) -> int:
+    return ((base * 1_000_003 + tensor_id) * 65_537 + sub + 1) & 0x7FFF_FFFF_FFFF_FFFF

@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(inkling_moe_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(inkling_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -137,3 +137,39 @@ def test_strerror(lib):
     for c in (0, -1, -2, -3, -4, -99):
         assert isinstance(lib.inkling_moe_strerror(c), bytes)
     assert lib.inkling_moe_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), B.INKLING_ERR_INVALID_ARGUMENT),
+    (dict(hidden=0), B.INKLING_ERR_INVALID_ARGUMENT),
+    (dict(intermediate=0), B.INKLING_ERR_INVALID_ARGUMENT),
+    (dict(dtype=5), B.INKLING_ERR_UNSUPPORTED),
+    (dict(out_dtype=5), B.INKLING_ERR_UNSUPPORTED),
+    (dict(hidden=96), B.INKLING_ERR_UNSUPPORTED),
+    (dict(intermediate=160), B.INKLING_ERR_UNSUPPORTED),
+])
+def test_dense_invalid_dims_rejected(lib, kw, code):
+    d = dict(T=64, hidden=128, intermediate=256, dtype=B.INKLING_BF16, out_dtype=B.INKLING_BF16)
+    d.update(kw)
+    dims = B.DenseDims(d["T"], d["hidden"], d["intermediate"], d["dtype"], d["out_dtype"])
+    n = ctypes.c_size_t(0)
+    assert lib.inkling_dense_mlp_workspace_size(ctypes.byref(dims), ctypes.byref(n)) == code
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.inkling_dense_mlp_forward(ctypes.byref(dims), fake, fake, fake, 1.0, ctypes.c_void_p(0x2000), fake,
+                                         1 << 40, None) == code
+
+
+def test_dense_pointer_and_workspace_checks(lib):
+    dims = B.DenseDims(64, 128, 256, B.INKLING_BF16, B.INKLING_BF16)
+    n = ctypes.c_size_t(0)
+    assert lib.inkling_dense_mlp_workspace_size(ctypes.byref(dims), ctypes.byref(n)) == B.INKLING_OK
+    # gamma + counters + act [T][I] bf16 + fp32 rows [T][H]
+    assert n.value >= 64 * 256 * 2 + 64 * 128 * 4
+    x, w, out, ws = (ctypes.c_void_p(v) for v in (0x1000, 0x2000, 0x3000, 0x4000))
+    f = lib.inkling_dense_mlp_forward
+    assert f(ctypes.byref(dims), None, w, w, 1.0, out, ws, n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(dims), x, None, w, 1.0, out, ws, n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(dims), x, w, w, 1.0, x, ws, n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(dims), x, w, w, 1.0, out, ws, n.value - 1, None) == B.INKLING_ERR_WORKSPACE
+    zero = B.DenseDims(0, 128, 256, B.INKLING_BF16, B.INKLING_BF16)
+    assert f(ctypes.byref(zero), None, None, None, 1.0, None, None, 0, None) == B.INKLING_OK

@@ -199,3 +199,40 @@ def test_inkling_default_h6144():
     finally:
         del experts
         torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- InklingDenseMLP
+
+DENSE = {
+    "dense_bf16": wl.dense_custom("dense_bf16", T=200, hidden=256, intermediate=192, global_scale=0.75),
+    "dense_f32": wl.dense_custom("dense_f32", T=70, hidden=128, intermediate=128, dtype="f32", global_scale=1.25),
+    "dense_few_tokens": wl.dense_custom("dense_few_tokens", T=5, hidden=192, intermediate=320),
+}
+
+
+def _dense_check(w, rows=None):
+    inp = wl.dense_inputs(w, device=DEV)
+    out32 = B.dense_mlp_forward(inp["x"], inp["gate_up"], inp["down"], w.global_scale, out_dtype=torch.float32)
+    if w.dtype == "bf16":
+        out16 = B.dense_mlp_forward(inp["x"], inp["gate_up"], inp["down"], w.global_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out16, out32.to(torch.bfloat16)), "bf16 output is not the rounded fp32 output"
+    torch.cuda.synchronize()
+    x = P.host(inp["x"]) if rows is None else P.host(inp["x"][rows])
+    ref = oracle.dense_mlp(x, P.host(inp["gate_up"]), P.host(inp["down"]), w.global_scale)
+    rel = P.check_output(out32, ref, w.dtype, rows=rows)
+    _say(f"[parity] {w.name} ok: max_err/rms={rel:.2e}")
+
+
+@pytest.mark.parametrize("name", list(DENSE))
+def test_dense_mlp(name):
+    _dense_check(DENSE[name])
+
+
+def test_dense_mlp_h6144():
+    """The first Inkling layer's dense MLP (intermediate 24576) at hidden 6144,
+    T=8192; sampled tokens against the oracle."""
+    w = wl.DENSE_WORKLOADS["dense_h6144"]
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, w.T - 2, w.T - 1] + rng.choice(w.T, size=12, replace=False).tolist()))
+    _dense_check(w, rows=rows)
