@@ -189,7 +189,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the InklingDenseMLP line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
