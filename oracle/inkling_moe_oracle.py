@@ -21,6 +21,11 @@ What it computes follows the Inkling layers page
     input; padded tokens are excluded from routed dispatch.
   * InklingDenseMLP: the dense SwiGLU MLP on the same interleaved layout,
     scaled by its global_scale parameter.
+  * The backward of InklingMoE.forward: gradients of <dout, out> with respect
+    to the hidden states, the gate bank and every expert weight, by the chain
+    rule through the down projection, SwiGLU, the gate_up projection and the
+    log-sigmoid softmax of the gate (the correction bias only moves the
+    selection and gets no gradient).
 
 Everything runs in float64 on the exact input values (bf16 and fp32 inputs widen
 to fp64 without error, and their pairwise products are exact in fp64), with
@@ -41,7 +46,8 @@ log-sigmoid softmax, gammas summing to route_scale*global_scale, the
 interleaved SwiGLU against the de-interleaved textbook form, a one-expert top-1
 MoE against a dense SwiGLU MLP, token independence, expert relabelling, a
 hand-derived worked example (test_hand_derived_example), and the dense MLP
-against the textbook SwiGLU and against a one-expert top-1 MoE.  Agreement with
+against the textbook SwiGLU and against a one-expert top-1 MoE; the backward
+against central finite differences of the forward oracle for every input.  Agreement with
 the HuggingFace InklingTopkRouter or a real checkpoint: parity unpinned (neither
 exists here).
 """
@@ -259,3 +265,134 @@ def dense_mlp(x, w_gu, w_d, global_scale: float) -> np.ndarray:
     where global_scale enters; it is read as scaling the MLP output (equal in
     exact arithmetic to scaling the activation, since down_proj is linear)."""
     return float(global_scale) * expert_ffn(x, w_gu, w_d)
+
+
+# --------------------------------------------------------------------------
+# Backward of InklingMoE.forward (gradients of L = <dout, out>)
+# --------------------------------------------------------------------------
+
+def silu_grad(v) -> np.ndarray:
+    """d silu(v) / dv = sigma(v) * (1 + v * (1 - sigma(v)))."""
+    v = _f64(v)
+    s = sigmoid(v)
+    return s * (1.0 + v * (1.0 - s))
+
+
+def expert_backward(rows, w_gu, w_d, gammas, dout_rows):
+    """Backward of gamma * down(swiglu(gate_up(rows))) for the rows one expert
+    received.  Returns (d rows [n, H], d gate_up [2I, H], d down [H, I],
+    d gammas [n])."""
+    X, Wgu, Wd, G = _f64(rows), _f64(w_gu), _f64(w_d), _f64(dout_rows)
+    gam = _f64(gammas)
+    h = X @ Wgu.T
+    g, u = h[:, 0::2], h[:, 1::2]
+    p = silu(g) * u                       # activation before the routing weight
+    a = p * gam[:, None]                  # activation the down projection sees
+    da = G @ Wd                           # [n, I]
+    d_wd = G.T @ a                        # [H, I]
+    d_gam = np.sum(da * p, axis=1)
+    dp = da * gam[:, None]
+    dh = np.empty_like(h)
+    dh[:, 0::2] = dp * u * silu_grad(g)
+    dh[:, 1::2] = dp * silu(g)
+    return dh @ Wgu, dh.T @ X, d_wd, d_gam
+
+
+def router_backward(z, bias, n_routed: int, topk_indices, topk_weights, shared_gammas, d_topk_weights,
+                    d_shared_gammas, route_scale: float, global_scale: float):
+    """Gradient of the gate logits z [T, E+S] from the gradients of the
+    returned weights.  gamma = c * softmax(l), c = route_scale * global_scale,
+    l_j = log sigmoid(z_j) over the selected routed and the shared logits, so
+    dl_j = q_j (c dgamma_j - sum_m q_m c dgamma_m) with q = gamma / c, and
+    dz_j = dl_j (1 - sigma(z_j)).  Unselected routed logits and the correction
+    bias, which only moves the selection, get no gradient."""
+    z = _f64(z)
+    T = z.shape[0]
+    E = n_routed
+    c = float(route_scale) * float(global_scale)
+    zj = np.concatenate([np.take_along_axis(z[:, :E], topk_indices, axis=1), z[:, E:]], axis=1)
+    q = np.concatenate([_f64(topk_weights), _f64(shared_gammas)], axis=1) / c
+    dq = c * np.concatenate([_f64(d_topk_weights), _f64(d_shared_gammas)], axis=1)
+    dl = q * (dq - np.sum(q * dq, axis=1, keepdims=True))
+    dzj = dl * (1.0 - sigmoid(zj))
+    dz = np.zeros_like(z)
+    k = topk_indices.shape[1]
+    np.add.at(dz, (np.repeat(np.arange(T), k), topk_indices.reshape(-1)), dzj[:, :k].reshape(-1))
+    dz[:, E:] = dzj[:, k:]
+    return dz
+
+
+def moe_backward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int, route_scale: float,
+                 global_scale: float, dout, padding_mask=None, routing=None, tokens=None, experts=None):
+    """Gradients of L = sum(dout * InklingMoE.forward(x)) in fp64.
+
+    Returns a dict:
+      dx [T or len(tokens), H]; d_gate_bank [E+S, H] (only when tokens is None);
+      d_w_gu {e: [2I, H]}, d_w_d {e: [H, I]} for the routed experts in
+      `experts` (default all; an expert that received no token has zero
+      gradients); d_wsh_gu [S, 2I, H], d_wsh_d [S, H, I]; dz [T', E+S];
+      d_topk_weights [T', k], d_shared_gammas [T', S].
+    Padded tokens skip the routed experts (their routed weights get no
+    gradient) and keep the shared experts."""
+    x, G = _f64(x), _f64(dout)
+    T, H = x.shape
+    E = _f64(bias).shape[0]
+    S = len(wsh_gu)
+    if routing is None:
+        z = gate_logits(x, gate_bank)
+        tw, ti, sg, s = route(z, bias, E, top_k, route_scale, global_scale)
+        routing = dict(logits=z, topk_weights=tw, topk_indices=ti, shared_gammas=sg)
+    z, tw, ti, sg = routing["logits"], routing["topk_weights"], routing["topk_indices"], routing["shared_gammas"]
+    pad = np.zeros(T, dtype=bool) if padding_mask is None else np.asarray(padding_mask, dtype=bool)
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    want = range(E) if experts is None else [int(e) for e in experts]
+    R = len(rows)
+    dx = np.zeros((R, H), dtype=F64)
+    d_tw = np.zeros((R, top_k), dtype=F64)
+    d_sg = np.zeros((R, S), dtype=F64)
+    res = {"d_w_gu": {}, "d_w_d": {}}
+    # routed experts: pairs (local row, choice) of the rows asked for
+    lt_all, li_all = np.nonzero(~pad[rows][:, None] & (ti[rows] >= 0))
+    e_all = ti[rows][lt_all, li_all]
+    for e in np.unique(e_all):
+        m = e_all == e
+        lt, li = lt_all[m], li_all[m]
+        dX, dgu, dd, dgam = expert_backward(x[rows][lt], w_gu[e], w_d[e], tw[rows][lt, li], G[rows][lt])
+        np.add.at(dx, lt, dX)
+        d_tw[lt, li] = dgam
+        if tokens is None:
+            res["d_w_gu"][int(e)], res["d_w_d"][int(e)] = dgu, dd
+    # weight gradients of the asked experts over every token (when rows was a subset)
+    for e in want:
+        if e in res["d_w_gu"]:
+            continue
+        t_e, i_e = np.nonzero(~pad[:, None] & (ti == e))
+        if len(t_e) == 0:
+            res["d_w_gu"][e] = np.zeros_like(_f64(w_gu[e]))
+            res["d_w_d"][e] = np.zeros_like(_f64(w_d[e]))
+            continue
+        _, dgu, dd, _ = expert_backward(x[t_e], w_gu[e], w_d[e], tw[t_e, i_e], G[t_e])
+        res["d_w_gu"][e], res["d_w_d"][e] = dgu, dd
+    if experts is not None:
+        res["d_w_gu"] = {e: res["d_w_gu"][e] for e in want}
+        res["d_w_d"] = {e: res["d_w_d"][e] for e in want}
+    # shared experts: every token
+    d_wsh_gu, d_wsh_d = [], []
+    for s in range(S):
+        if tokens is None:
+            dX, dgu, dd, dgam = expert_backward(x, wsh_gu[s], wsh_d[s], sg[:, s], G)
+        else:
+            dX, _, _, dgam = expert_backward(x[rows], wsh_gu[s], wsh_d[s], sg[rows, s], G[rows])
+            _, dgu, dd, _ = expert_backward(x, wsh_gu[s], wsh_d[s], sg[:, s], G)
+        dx += dX
+        d_sg[:, s] = dgam
+        d_wsh_gu.append(dgu)
+        d_wsh_d.append(dd)
+    # router
+    dz = router_backward(z[rows], bias, E, ti[rows], tw[rows], sg[rows], d_tw, d_sg, route_scale, global_scale)
+    dx += dz @ _f64(gate_bank)
+    res.update(dx=dx, dz=dz, d_topk_weights=d_tw, d_shared_gammas=d_sg,
+               d_wsh_gu=np.array(d_wsh_gu).reshape((S,) + np.shape(_f64(wsh_gu[0])) if S else (0,)),
+               d_wsh_d=np.array(d_wsh_d).reshape((S,) + np.shape(_f64(wsh_d[0])) if S else (0,)))
+    res["d_gate_bank"] = dz.T @ x if tokens is None else None
+    return res

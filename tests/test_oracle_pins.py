@@ -375,3 +375,93 @@ def test_dense_mlp_equals_one_expert_moe_with_route_scale_as_global_scale():
     bias = rng.standard_normal(1)
     moe, _ = oracle.moe_forward(x, bank, bias, w_gu, w_d, [], [], 1, 2.0, 0.625)
     assert np.allclose(moe, oracle.dense_mlp(x, w_gu[0], w_d[0], 1.25), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- backward
+
+def _bw_case(seed, T=3, H=6, E=4, k=2, S=1, I=3, rs=1.7, gs=0.9):
+    rng = np.random.default_rng(seed)
+    c = dict(x=rng.standard_normal((T, H)), bank=rng.standard_normal((E + S, H)) * 0.5,
+             bias=rng.standard_normal(E) * 0.1, w_gu=rng.standard_normal((E, 2 * I, H)) * 0.4,
+             w_d=rng.standard_normal((E, H, I)) * 0.4, wsh_gu=rng.standard_normal((S, 2 * I, H)) * 0.4,
+             wsh_d=rng.standard_normal((S, H, I)) * 0.4, dout=rng.standard_normal((T, H)), k=k, rs=rs, gs=gs)
+    return c
+
+
+def _loss(c, pad=None, **over):
+    p = dict(c)
+    p.update(over)
+    out, _ = oracle.moe_forward(p["x"], p["bank"], p["bias"], p["w_gu"], p["w_d"], p["wsh_gu"], p["wsh_d"],
+                                p["k"], p["rs"], p["gs"], padding_mask=pad)
+    return float(np.sum(out * p["dout"]))
+
+
+def _fd_grad(c, name, pad=None, eps=1e-6):
+    base = c[name]
+    g = np.zeros_like(base)
+    for idx in np.ndindex(base.shape):
+        hi, lo = base.copy(), base.copy()
+        hi[idx] += eps
+        lo[idx] -= eps
+        g[idx] = (_loss(c, pad, **{name: hi}) - _loss(c, pad, **{name: lo})) / (2 * eps)
+    return g
+
+
+def _margins_clear(c, tol=1e-3):
+    z = oracle.gate_logits(c["x"], c["bank"])
+    s = oracle.selection_scores(z[:, :c["bias"].shape[0]], c["bias"])
+    return np.all(oracle.topk_margin(s, c["k"]) > tol)
+
+
+@pytest.mark.parametrize("seed,kw,padded", [
+    (31, {}, False),
+    (32, dict(S=2, k=1), False),
+    (33, dict(S=0, k=2), False),
+    (38, {}, True),
+])
+def test_backward_matches_finite_differences(seed, kw, padded):
+    """Every gradient of L = <dout, out> against central differences of the
+    forward oracle (the selection does not change under the perturbation: all
+    top-k margins exceed 1e-3)."""
+    c = _bw_case(seed, **kw)
+    assert _margins_clear(c)
+    pad = np.array([False, True, False]) if padded else None
+    g = oracle.moe_backward(c["x"], c["bank"], c["bias"], c["w_gu"], c["w_d"], c["wsh_gu"], c["wsh_d"], c["k"],
+                            c["rs"], c["gs"], c["dout"], padding_mask=pad)
+    E = c["bias"].shape[0]
+    checks = [("x", g["dx"]), ("bank", g["d_gate_bank"]),
+              ("w_gu", np.stack([g["d_w_gu"][e] for e in range(E)])),
+              ("w_d", np.stack([g["d_w_d"][e] for e in range(E)]))]
+    if c["wsh_gu"].shape[0]:
+        checks += [("wsh_gu", g["d_wsh_gu"]), ("wsh_d", g["d_wsh_d"])]
+    for name, analytic in checks:
+        fd = _fd_grad(c, name, pad)
+        assert np.allclose(analytic, fd, rtol=1e-6, atol=1e-8), name
+    # the correction bias only moves the selection: its finite difference is 0
+    assert np.allclose(_fd_grad(c, "bias", pad), 0.0, atol=1e-8)
+
+
+def test_backward_token_and_expert_subsets_agree_with_full():
+    c = _bw_case(35, T=6, E=5, k=2, S=1)
+    args = (c["x"], c["bank"], c["bias"], c["w_gu"], c["w_d"], c["wsh_gu"], c["wsh_d"], c["k"], c["rs"], c["gs"],
+            c["dout"])
+    full = oracle.moe_backward(*args)
+    part = oracle.moe_backward(*args, tokens=[4, 1], experts=[3, 0])
+    assert np.allclose(part["dx"], full["dx"][[4, 1]], rtol=1e-13, atol=1e-14)
+    assert np.allclose(part["dz"], full["dz"][[4, 1]], rtol=1e-13, atol=1e-14)
+    for e in (3, 0):
+        assert np.allclose(part["d_w_gu"][e], full["d_w_gu"][e], rtol=1e-13, atol=1e-14)
+        assert np.allclose(part["d_w_d"][e], full["d_w_d"][e], rtol=1e-13, atol=1e-14)
+    assert np.allclose(part["d_wsh_gu"], full["d_wsh_gu"], rtol=1e-13, atol=1e-14)
+    assert part["d_gate_bank"] is None
+
+
+def test_router_backward_weights_sum_rule():
+    """The gammas sum to rs*gs, so dout-independent: a dgamma that is the same
+    for every expert of a token gives dz = 0."""
+    c = _bw_case(36, T=4, E=5, k=2, S=2)
+    z = oracle.gate_logits(c["x"], c["bank"])
+    tw, ti, sg, _ = oracle.route(z, c["bias"], 5, 2, c["rs"], c["gs"])
+    const = np.full((4, 2), 0.37)
+    dz = oracle.router_backward(z, c["bias"], 5, ti, tw, sg, const, np.full((4, 2), 0.37), c["rs"], c["gs"])
+    assert np.allclose(dz, 0.0, atol=1e-14)
