@@ -144,6 +144,33 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
                         void* stream);
 
 /*
+ * Backward of InklingMoE.forward: gradients of L = sum(dout * out) for the
+ * layer as inkling_moe_forward computes it (chain rule through the down
+ * projection, SwiGLU, the gate_up projection and the gate's log-sigmoid
+ * softmax; the correction bias only moves the top-k selection and has no
+ * gradient; padded tokens skip the routed experts and keep the shared ones).
+ * The routing, the gate_up activations and the permutation are recomputed
+ * from x.  Every gradient buffer is overwritten, not accumulated; an expert
+ * that receives no token gets zeros.
+ *   dout [T][hidden] (dims->dtype);  dx [T][hidden] (dims->out_dtype), which
+ *   must alias neither x nor dout.
+ * Weight gradients are fp32 with the weights' layouts.
+ */
+typedef struct {
+    float* d_gate_bank;        /* [n_routed + n_shared][hidden] */
+    float* d_routed_gate_up;   /* [n_routed][2*I][hidden]       */
+    float* d_routed_down;      /* [n_routed][hidden][I]         */
+    float* d_shared_gate_up;   /* [n_shared][2*I][hidden] (NULL iff n_shared == 0) */
+    float* d_shared_down;      /* [n_shared][hidden][I]         */
+} inkling_moe_grads_t;
+
+int inkling_moe_backward_workspace_size(const inkling_moe_dims_t* dims, size_t* bytes);
+
+int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                         const inkling_experts_t* experts, const uint8_t* padding_mask, const void* dout, void* dx,
+                         inkling_moe_grads_t* grads, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * InklingDenseMLP (layers page): the dense SwiGLU MLP on the fused interleaved
  * gate_up layout, scaled by the module's global_scale:
  *   out = global_scale * down . (silu(gate) * up),  [gate, up] = gate_up . x

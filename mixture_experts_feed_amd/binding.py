@@ -25,7 +25,8 @@ INKLING_BF16 = 1
 
 EXPORTED = ("inkling_moe_workspace_size", "inkling_moe_route", "inkling_moe_forward",
             "inkling_moe_strerror", "inkling_moe_last_hip_error", "inkling_moe_set_stage_events",
-            "inkling_dense_mlp_workspace_size", "inkling_dense_mlp_forward")
+            "inkling_dense_mlp_workspace_size", "inkling_dense_mlp_forward",
+            "inkling_moe_backward_workspace_size", "inkling_moe_backward")
 INKLING_STAGE_EVENTS = 7
 STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "combine")
 
@@ -39,6 +40,12 @@ class Dims(ctypes.Structure):
 class DenseDims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [("d_gate_bank", ctypes.c_void_p), ("d_routed_gate_up", ctypes.c_void_p),
+                ("d_routed_down", ctypes.c_void_p), ("d_shared_gate_up", ctypes.c_void_p),
+                ("d_shared_down", ctypes.c_void_p)]
 
 
 class Gate(ctypes.Structure):
@@ -99,6 +106,12 @@ def load() -> ctypes.CDLL:
                                               ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_size_t, ctypes.c_void_p]
     lib.inkling_dense_mlp_forward.restype = ctypes.c_int
+    lib.inkling_moe_backward_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)]
+    lib.inkling_moe_backward_workspace_size.restype = ctypes.c_int
+    lib.inkling_moe_backward.argtypes = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.POINTER(Gate),
+                                         ctypes.POINTER(Experts), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.POINTER(Grads), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.inkling_moe_backward.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -287,3 +300,53 @@ def dense_mlp_forward(x: torch.Tensor, gate_up: torch.Tensor, down: torch.Tensor
     if rc != INKLING_OK:
         raise InklingError(rc, "inkling_dense_mlp_forward")
     return out
+
+
+def backward_workspace_size(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().inkling_moe_backward_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    if rc != INKLING_OK:
+        raise InklingError(rc, "inkling_moe_backward_workspace_size")
+    return int(n.value)
+
+
+def backward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: torch.Tensor, w_d: torch.Tensor,
+             wsh_gu: Optional[torch.Tensor], wsh_d: Optional[torch.Tensor], top_k: int, route_scale: float,
+             global_scale: float, dout: torch.Tensor, padding_mask: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, dx_dtype: Optional[torch.dtype] = None,
+             grads: Optional[dict] = None) -> dict:
+    """inkling_moe_backward: dict(dx, d_gate_bank, d_w_gu, d_w_d, d_wsh_gu, d_wsh_d)."""
+    T, H = x.shape
+    E, twoI, _ = w_gu.shape
+    S = 0 if wsh_gu is None else wsh_gu.shape[0]
+    for t, n in ((x, "x"), (w_gu, "w_gu"), (w_d, "w_d"), (dout, "dout")):
+        _need(t, n, x.dtype)
+    if S:
+        _need(wsh_gu, "wsh_gu", x.dtype)
+        _need(wsh_d, "wsh_d", x.dtype)
+    _need(gate_bank, "gate_bank", torch.float32)
+    _need(bias, "bias", torch.float32)
+    dx_dtype = x.dtype if dx_dtype is None else dx_dtype
+    dims = make_dims(T, H, E, top_k, S, twoI // 2, x.dtype, dx_dtype)
+    dev = x.device
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        grads = {"dx": torch.empty((T, H), dtype=dx_dtype, device=dev),
+                 "d_gate_bank": torch.empty(tuple(gate_bank.shape), **f32),
+                 "d_w_gu": torch.empty(tuple(w_gu.shape), **f32), "d_w_d": torch.empty(tuple(w_d.shape), **f32),
+                 "d_wsh_gu": torch.empty(tuple(wsh_gu.shape), **f32) if S else None,
+                 "d_wsh_d": torch.empty(tuple(wsh_d.shape), **f32) if S else None}
+    g = Grads(_ptr(grads["d_gate_bank"]), _ptr(grads["d_w_gu"]), _ptr(grads["d_w_d"]), _ptr(grads["d_wsh_gu"]),
+              _ptr(grads["d_wsh_d"]))
+    gate = Gate(gate_bank.data_ptr(), bias.data_ptr(), float(route_scale), float(global_scale))
+    ex = Experts(w_gu.data_ptr(), w_d.data_ptr(), _ptr(wsh_gu) if S else None, _ptr(wsh_d) if S else None)
+    if padding_mask is not None:
+        _need(padding_mask, "padding_mask", torch.uint8)
+    if workspace is None:
+        workspace = torch.empty(max(1, backward_workspace_size(dims)), dtype=torch.uint8, device=dev)
+    rc = load().inkling_moe_backward(ctypes.byref(dims), x.data_ptr(), ctypes.byref(gate), ctypes.byref(ex),
+                                     _ptr(padding_mask), dout.data_ptr(), grads["dx"].data_ptr(), ctypes.byref(g),
+                                     workspace.data_ptr(), workspace.numel(), _stream(dev))
+    if rc != INKLING_OK:
+        raise InklingError(rc, "inkling_moe_backward")
+    return grads

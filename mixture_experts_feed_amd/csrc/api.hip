@@ -143,6 +143,61 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
 
 }  // namespace
 
+// ---- backward -----------------------------------------------------------------
+struct BwdLayout {
+    Layout F;   // the forward's routing and row buffers (y / ysh hold the dx rows)
+    int Cmax, Tpad;
+    size_t h_r, h_sh, dh_r, dh_sh, wdT, wshdT, wguT, wshguT, dgp_r, dgp_sh, dz, dzc, poff, col_row, col_tok;
+    size_t GsT, xsT, aT, dhT, GT, xT, a_shT, dh_shT, total;
+};
+
+BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
+    BwdLayout B = {};
+    B.F = make_layout(d);
+    // every backward GEMM uses the 256x256 tiles (the activation-gradient
+    // epilogue sums 64-column slices per wave), so the routed tile list is
+    // built for 256-row tiles
+    B.F.cfg = 0;
+    B.F.bm = gemm_cfg_bm(0);
+    B.F.max_tiles = (int)((d->T * d->top_k + B.F.bm - 1) / B.F.bm) + d->n_routed;
+    const size_t T = (size_t)d->T, E = d->n_routed, S = d->n_shared, k = d->top_k, H = d->hidden, I = d->intermediate;
+    const size_t es = d->dtype == INKLING_BF16 ? 2 : 4;
+    B.Cmax = (int)((T * k + 64 * E + 63) / 64 * 64);
+    B.Tpad = (int)((T + 63) / 64 * 64);
+    const size_t C = (size_t)B.Cmax, Tp = (size_t)B.Tpad;
+    size_t o = B.F.total;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    B.h_r = take(T * k * 2 * I * 4);
+    B.h_sh = take(T * S * 2 * I * 4);
+    B.dh_r = take(T * k * 2 * I * es);
+    B.dh_sh = take(T * S * 2 * I * es);
+    B.wdT = take(E * I * H * es);
+    B.wshdT = take(S * I * H * es);
+    B.wguT = take(E * 2 * I * H * es);
+    B.wshguT = take(S * 2 * I * H * es);
+    B.dgp_r = take(T * k * (I / 64) * 4);
+    B.dgp_sh = take(T * S * (I / 64) * 4);
+    B.dz = take(T * (E + S) * 4);
+    B.dzc = take(T * (k + S) * 4);
+    B.poff = take((E + 1) * 4);
+    B.col_row = take(C * 4);
+    B.col_tok = take(C * 4);
+    B.GsT = take(H * C * es);
+    B.xsT = take(H * C * es);
+    B.aT = take(I * C * es);
+    B.dhT = take(2 * I * C * es);
+    B.GT = take(H * Tp * es);
+    B.xT = take(H * Tp * es);
+    B.a_shT = take(S * I * Tp * es);
+    B.dh_shT = take(S * 2 * I * Tp * es);
+    B.total = o;
+    return B;
+}
+
 // ---- InklingDenseMLP ------------------------------------------------------
 int check_dense_dims(const inkling_dense_dims_t* d) {
     if (d == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
@@ -322,6 +377,197 @@ int inkling_dense_mlp_forward(const inkling_dense_dims_t* dims, const void* x, c
     HIP_TRY(launch_gate_up(p, s));
     HIP_TRY(launch_down(p, s));
     HIP_TRY(launch_combine(p, s));
+    return INKLING_OK;
+}
+
+int inkling_moe_backward_workspace_size(const inkling_moe_dims_t* dims, size_t* bytes) {
+    const int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (bytes == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    *bytes = make_bwd_layout(dims).total;
+    return INKLING_OK;
+}
+
+int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                         const inkling_experts_t* w, const uint8_t* padding_mask, const void* dout, void* dx,
+                         inkling_moe_grads_t* g, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (dims->T == 0) return INKLING_OK;
+    if (x == nullptr || dout == nullptr || dx == nullptr || check_gate(gate) != INKLING_OK || w == nullptr ||
+        g == nullptr)
+        return INKLING_ERR_INVALID_ARGUMENT;
+    const int S = dims->n_shared;
+    if (w->routed_gate_up == nullptr || w->routed_down == nullptr ||
+        (S > 0 && (w->shared_gate_up == nullptr || w->shared_down == nullptr)))
+        return INKLING_ERR_INVALID_ARGUMENT;
+    if (g->d_gate_bank == nullptr || g->d_routed_gate_up == nullptr || g->d_routed_down == nullptr ||
+        (S > 0 && (g->d_shared_gate_up == nullptr || g->d_shared_down == nullptr)))
+        return INKLING_ERR_INVALID_ARGUMENT;
+    if (dx == x || dx == dout) return INKLING_ERR_INVALID_ARGUMENT;
+    const BwdLayout B = make_bwd_layout(dims);
+    const Layout& L = B.F;
+    if (workspace == nullptr || workspace_bytes < B.total) return INKLING_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const int T = (int)dims->T, E = dims->n_routed, k = dims->top_k, H = dims->hidden, I = dims->intermediate;
+    const int dt = dims->dtype == INKLING_BF16 ? 1 : 0;
+
+    // 1. routing and permutation, as in the forward
+    RouteBufs rb = {};
+    rb.topk_idx = at<int32_t>(workspace, L.topk_idx);
+    rb.topk_w = at<float>(workspace, L.topk_w);
+    rb.shared_g = at<float>(workspace, L.shared_g);
+    rb.counts = at<int32_t>(workspace, L.counts);
+    rb.offsets = at<int32_t>(workspace, L.offsets);
+    rb.sorted_slots = at<int32_t>(workspace, L.sorted_slots);
+    rb.row_token = at<int32_t>(workspace, L.row_token);
+    rb.row_gamma = at<float>(workspace, L.row_gamma);
+    rb.pos = at<int32_t>(workspace, L.pos);
+    rb.tiles = at<RoutedTile>(workspace, L.tiles);
+    rb.num_tiles = at<int32_t>(workspace, L.num_tiles);
+    rc = run_route(dims, L, x, gate, padding_mask, rb, true, workspace, s);
+    if (rc != INKLING_OK) return rc;
+    int32_t* poff = at<int32_t>(workspace, B.poff);
+    int32_t* col_row = at<int32_t>(workspace, B.col_row);
+    int32_t* col_tok = at<int32_t>(workspace, B.col_tok);
+    HIP_TRY(launch_column_map(rb.counts, rb.offsets, rb.row_token, E, B.Cmax, poff, col_row, col_tok, s));
+
+    MoeGemmParams p = {};
+    p.dtype = dt;
+    p.out_dtype = dims->out_dtype == INKLING_BF16 ? 1 : 0;
+    p.cfg = L.cfg;
+    p.T = T;
+    p.H = H;
+    p.E = E;
+    p.S = S;
+    p.I = I;
+    p.k = k;
+    p.x = x;
+    p.w_gu = w->routed_gate_up;
+    p.w_d = w->routed_down;
+    p.wsh_gu = w->shared_gate_up;
+    p.wsh_d = w->shared_down;
+    p.tiles = rb.tiles;
+    p.num_tiles = rb.num_tiles;
+    p.offsets = rb.offsets;
+    p.row_token = rb.row_token;
+    p.row_slot = rb.sorted_slots;
+    p.row_gamma = rb.row_gamma;
+    p.shared_g = rb.shared_g;
+    p.pos = rb.pos;
+    p.max_routed_tiles = L.max_tiles;
+    p.round_counters = at<int32_t>(workspace, L.round_counters);
+    p.has_routed = 1;
+
+    // 2. h = gate_up(x) per routed row and per token for the shared experts
+    void* h_r = at<void>(workspace, B.h_r);
+    void* h_sh = at<void>(workspace, B.h_sh);
+    HIP_TRY(launch_gate_up_raw(p, h_r, h_sh, s));
+
+    // 3. transposed down projections; dact and the SwiGLU backward
+    void* wdT = at<void>(workspace, B.wdT);
+    void* wshdT = at<void>(workspace, B.wshdT);
+    HIP_TRY(launch_gather_transpose(dt, w->routed_down, wdT, nullptr, H, H, I, E, (long long)H * I, (long long)I * H,
+                                    s));
+    if (S > 0)
+        HIP_TRY(launch_gather_transpose(dt, w->shared_down, wshdT, nullptr, H, H, I, S, (long long)H * I,
+                                        (long long)I * H, s));
+    BwdActBufs ab = {};
+    ab.wdT = wdT;
+    ab.wshdT = wshdT;
+    ab.dout = dout;
+    ab.h_r = h_r;
+    ab.h_sh = h_sh;
+    ab.dh_r = at<void>(workspace, B.dh_r);
+    ab.dh_sh = at<void>(workspace, B.dh_sh);
+    ab.a_r = at<void>(workspace, L.act_r);
+    ab.a_sh = at<void>(workspace, L.act_sh);
+    ab.dgp_r = at<float>(workspace, B.dgp_r);
+    ab.dgp_sh = at<float>(workspace, B.dgp_sh);
+    HIP_TRY(launch_dact(p, ab, s));
+
+    // 4. gate: dz of the selected and shared logits
+    float* dz = at<float>(workspace, B.dz);
+    float* dzc = at<float>(workspace, B.dzc);
+    HIP_TRY(launch_router_backward(at<double>(workspace, L.zpart), L.ksplit, rb.topk_idx, rb.pos, ab.dgp_r, ab.dgp_sh,
+                                   T, E, S, k, I, gate->route_scale, gate->global_scale, dz, dzc, s));
+
+    // 5. dx rows: transposed gate_up projections against dh (the down-GEMM shape,
+    //    K = 2I); then dx = shared + routed rows + gate term, rounded once
+    void* wguT = at<void>(workspace, B.wguT);
+    void* wshguT = at<void>(workspace, B.wshguT);
+    HIP_TRY(launch_gather_transpose(dt, w->routed_gate_up, wguT, nullptr, 2 * I, 2 * I, H, E, (long long)2 * I * H,
+                                    (long long)H * 2 * I, s));
+    if (S > 0)
+        HIP_TRY(launch_gather_transpose(dt, w->shared_gate_up, wshguT, nullptr, 2 * I, 2 * I, H, S,
+                                        (long long)2 * I * H, (long long)H * 2 * I, s));
+    MoeGemmParams q = p;
+    q.I = 2 * I;
+    q.w_d = wguT;
+    q.wsh_d = wshguT;
+    q.act_r = ab.dh_r;
+    q.act_sh = ab.dh_sh;
+    q.y = at<void>(workspace, L.y);
+    q.ysh = at<void>(workspace, L.ysh);
+    HIP_TRY(launch_down(q, s));
+    HIP_TRY(launch_dx_combine(p.out_dtype, at<float>(workspace, L.y), S > 0 ? at<float>(workspace, L.ysh) : nullptr,
+                              rb.pos, rb.topk_idx, dzc, gate->gate_bank, dx, T, H, E, S, k, s));
+
+    // 6. gate bank gradient
+    HIP_TRY(launch_dbank(dt, dz, x, T, H, E + S, g->d_gate_bank, s));
+
+    // 7. weight gradients: operands transposed so that K (rows of an expert,
+    //    each expert's columns padded to 64 with zeros; or tokens) is contiguous
+    const int C = B.Cmax, Tp = B.Tpad;
+    void* GsT = at<void>(workspace, B.GsT);
+    void* xsT = at<void>(workspace, B.xsT);
+    void* aT = at<void>(workspace, B.aT);
+    void* dhT = at<void>(workspace, B.dhT);
+    void* GT = at<void>(workspace, B.GT);
+    void* xT = at<void>(workspace, B.xT);
+    void* a_shT = at<void>(workspace, B.a_shT);
+    void* dh_shT = at<void>(workspace, B.dh_shT);
+    HIP_TRY(launch_gather_transpose(dt, dout, GsT, col_tok, 0, C, H, 1, 0, 0, s));
+    HIP_TRY(launch_gather_transpose(dt, x, xsT, col_tok, 0, C, H, 1, 0, 0, s));
+    HIP_TRY(launch_gather_transpose(dt, ab.a_r, aT, col_row, 0, C, I, 1, 0, 0, s));
+    HIP_TRY(launch_gather_transpose(dt, ab.dh_r, dhT, col_row, 0, C, 2 * I, 1, 0, 0, s));
+    if (S > 0) {
+        HIP_TRY(launch_gather_transpose(dt, dout, GT, nullptr, T, Tp, H, 1, 0, 0, s));
+        HIP_TRY(launch_gather_transpose(dt, x, xT, nullptr, T, Tp, H, 1, 0, 0, s));
+        HIP_TRY(launch_gather_transpose(dt, ab.a_sh, a_shT, nullptr, T, Tp, S * I, 1, 0, 0, s));
+        HIP_TRY(launch_gather_transpose(dt, ab.dh_sh, dh_shT, nullptr, T, Tp, S * 2 * I, 1, 0, 0, s));
+    }
+    WgradParams wd = {};   // d down[e][h][i] = sum_r dout[t(r)][h] a[r][i]
+    wd.dtype = dt;
+    wd.E = E;
+    wd.S = S;
+    wd.M = H;
+    wd.N = I;
+    wd.B_r = GsT;
+    wd.A_r = aT;
+    wd.poff = poff;
+    wd.ld_r = C;
+    wd.B_s = GT;
+    wd.A_s = a_shT;
+    wd.ld_s = Tp;
+    wd.K_s = Tp;
+    wd.a_sh_stride = (long long)I * Tp;
+    wd.b_sh_stride = 0;
+    wd.out_r = g->d_routed_down;
+    wd.out_s = g->d_shared_down;
+    HIP_TRY(launch_wgrad(wd, s));
+    WgradParams wg = wd;   // d gate_up[e][n][h] = sum_r dh[r][n] x[t(r)][h]
+    wg.M = 2 * I;
+    wg.N = H;
+    wg.B_r = dhT;
+    wg.A_r = xsT;
+    wg.B_s = dh_shT;
+    wg.A_s = xT;
+    wg.a_sh_stride = 0;
+    wg.b_sh_stride = (long long)2 * I * Tp;
+    wg.out_r = g->d_routed_gate_up;
+    wg.out_s = g->d_shared_gate_up;
+    HIP_TRY(launch_wgrad(wg, s));
     return INKLING_OK;
 }
 

@@ -1,0 +1,307 @@
+// Backward of the Inkling MoE feed-forward on gfx950: the kernels around the
+// grouped GEMMs (which live in gemm.hip).
+//
+// Gradients of L = <dout, out> follow the chain rule through the layer of the
+// Inkling layers page (InklingMoE.forward, InklingGate, inkling_swiglu,
+// InklingSharedExperts):
+//   per routed slot / shared expert: dact = down^T dout, dgamma = dact . p,
+//     dh = [dgate, dup] of the SwiGLU times gamma, dx += gate_up^T dh,
+//     d down += dout (x) a, d gate_up += dh (x) x;
+//   gate: gamma = c softmax(l), l_j = log sigmoid(z_j) over the selected
+//     routed and the shared logits, c = route_scale * global_scale:
+//     dz_j = q_j (c dgamma_j - sum_m q_m c dgamma_m) (1 - sigmoid(z_j)),
+//     dx += sum_j dz_j bank_j, d bank_j = sum_t dz_tj x_t.
+// The correction bias only moves the selection and has no gradient.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace inkling {
+
+namespace {
+
+constexpr int kTrTile = 64;
+
+// out_b[d][c] = src_b[row(c)][d] for d < D, c < C, with row(c) = map[c]
+// (map != NULL; -1 gives 0) or c (c < n_rows, else 0).  src rows have D
+// elements, out rows C.  64x64 tiles through LDS, 256 threads.
+template <typename TE>
+__global__ __launch_bounds__(256) void gather_transpose_kernel(const TE* __restrict__ src, TE* __restrict__ out,
+                                                               const int32_t* __restrict__ map, int n_rows, int C,
+                                                               int D, long long src_batch, long long out_batch) {
+    __shared__ TE tile[kTrTile][kTrTile + 1];
+    const int c0 = blockIdx.x * kTrTile, d0 = blockIdx.y * kTrTile;
+    src += blockIdx.z * src_batch;
+    out += blockIdx.z * out_batch;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    // read: rows c (one per iteration), columns d coalesced
+    for (int cc = ty; cc < kTrTile; cc += 4) {
+        const int c = c0 + cc;
+        int row = -1;
+        if (c < C) row = map ? map[c] : (c < n_rows ? c : -1);
+        const int d = d0 + tx;
+        tile[cc][tx] = (row >= 0 && d < D) ? src[(size_t)row * D + d] : (TE)0;
+    }
+    __syncthreads();
+    // write: rows d, columns c coalesced
+    for (int dd = ty; dd < kTrTile; dd += 4) {
+        const int d = d0 + dd, c = c0 + tx;
+        if (d < D && c < C) out[(size_t)d * C + c] = tile[tx][dd];
+    }
+}
+
+// poff[e] = sum over e' < e of counts rounded up to 64 (poff[E] the total);
+// one block.
+__global__ __launch_bounds__(1024) void padded_offsets_kernel(const int32_t* __restrict__ counts, int E,
+                                                              int32_t* __restrict__ poff) {
+    __shared__ int32_t sc[1024];
+    const int tid = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < E; base += 1024) {
+        const int e = base + tid;
+        const int v = e < E ? (counts[e] + 63) / 64 * 64 : 0;
+        sc[tid] = v;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {
+            const int o = tid >= d ? sc[tid - d] : 0;
+            __syncthreads();
+            sc[tid] += o;
+            __syncthreads();
+        }
+        if (e < E) poff[e] = carry + sc[tid] - v;
+        carry += sc[1023];
+        __syncthreads();
+    }
+    if (tid == 0) poff[E] = carry;
+}
+
+// For padded column c of expert e (poff[e] <= c < poff[e+1]): the sorted row
+// offsets[e] + (c - poff[e]) while inside the expert's count, else -1; and its
+// token.  Columns past poff[E] get -1.
+__global__ __launch_bounds__(256) void column_map_kernel(const int32_t* __restrict__ poff,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ row_token, int E, int C,
+                                                         int32_t* __restrict__ col_row,
+                                                         int32_t* __restrict__ col_tok) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    int row = -1;
+    if (c < poff[E]) {
+        int lo = 0, hi = E - 1;   // last e with poff[e] <= c
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (poff[mid] <= c) lo = mid;
+            else hi = mid - 1;
+        }
+        const int j = c - poff[lo];
+        if (j < offsets[lo + 1] - offsets[lo]) row = offsets[lo] + j;
+    }
+    col_row[c] = row;
+    col_tok[c] = row >= 0 ? row_token[row] : -1;
+}
+
+// One wave per token: routing-weight gradients (sums of the 64-column
+// partials in column order), then the gate-logit gradients of the k selected
+// routed and the S shared logits (fp64).  dz [T][E+S] (zeros elsewhere) and
+// the compact dzc [T][k+S] (selection order, then shared).
+__global__ __launch_bounds__(256) void router_backward_kernel(
+    const double* __restrict__ zpart, int ksplit, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ pos, const float* __restrict__ dgp_r, const float* __restrict__ dgp_sh, int T, int E,
+    int S, int k, int I, double scale, float* __restrict__ dz, float* __restrict__ dzc) {
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;   // wave-uniform
+    const int NE = E + S, nj = k + S, chunks = I / 64;
+    // lane j < k + S: expert e_j, its logit, its routing-weight gradient
+    double zj = 0.0, dg = 0.0;
+    int ej = -1;
+    if (lane < nj) {
+        if (lane < k) {
+            ej = topk_idx[(size_t)t * k + lane];
+            const int row = pos[(size_t)t * k + lane];
+            if (row >= 0)
+                for (int c = 0; c < chunks; ++c) dg += (double)dgp_r[(size_t)row * chunks + c];
+        } else {
+            const int s = lane - k;
+            ej = E + s;
+            for (int c = 0; c < chunks; ++c) dg += (double)dgp_sh[((size_t)t * S + s) * chunks + c];
+        }
+        for (int s = 0; s < ksplit; ++s) zj += zpart[((size_t)s * T + t) * NE + ej];
+    }
+    // q_j = sigmoid(z_j) / sum sigmoid (the log-sigmoid softmax in closed form)
+    const double sg = lane < nj ? 1.0 / (1.0 + exp(-zj)) : 0.0;
+    double ssum = sg;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off);
+    const double q = sg / ssum;
+    const double dq = scale * dg;
+    double qdq = q * dq;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) qdq += __shfl_xor(qdq, off);
+    const double dzj = lane < nj ? q * (dq - qdq) * (1.0 - sg) : 0.0;
+    if (lane < nj) dzc[(size_t)t * nj + lane] = (float)dzj;
+    // dense row: lane owns columns base + lane (the trip counts are uniform
+    // over the wave, so every shuffle has all lanes active); the selected
+    // routed experts are distinct
+    for (int base = 0; base < NE; base += 64) {
+        const int e = base + lane;
+        float v = 0.f;
+        for (int j = 0; j < nj; ++j) {
+            const int ejj = __shfl(ej, j);
+            const double dv = __shfl(dzj, j);
+            if (ejj == e) v = (float)dv;
+        }
+        if (e < NE) dz[(size_t)t * NE + e] = v;
+    }
+}
+
+// dx[t][h] = dx_sh[t][h] + sum over dispatched slots of dxr[t*k+i][h]
+//            + sum over j < k+S of dzc[t][j] * bank[e_j][h]; rounded once.
+template <typename TO>
+__global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict__ dxr, const float* __restrict__ dxs,
+                                                         const int32_t* __restrict__ pos,
+                                                         const int32_t* __restrict__ topk_idx,
+                                                         const float* __restrict__ dzc,
+                                                         const float* __restrict__ bank, TO* __restrict__ dx, int T,
+                                                         int H, int E, int S, int k) {
+    const int hq = H >> 2, nj = k + S;
+    const size_t total = (size_t)T * hq;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(idx / hq);
+        const int c = (int)(idx - (size_t)t * hq) * 4;
+        float4 s = dxs ? *reinterpret_cast<const float4*>(dxs + (size_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < k; ++i) {
+            if (pos[(size_t)t * k + i] >= 0) {
+                const float4 v = *reinterpret_cast<const float4*>(dxr + ((size_t)t * k + i) * H + c);
+                s.x += v.x;
+                s.y += v.y;
+                s.z += v.z;
+                s.w += v.w;
+            }
+        }
+        for (int j = 0; j < nj; ++j) {
+            const int e = j < k ? topk_idx[(size_t)t * k + j] : E + (j - k);
+            const float g = dzc[(size_t)t * nj + j];
+            const float4 b = *reinterpret_cast<const float4*>(bank + (size_t)e * H + c);
+            s.x += g * b.x;
+            s.y += g * b.y;
+            s.z += g * b.z;
+            s.w += g * b.w;
+        }
+        float w[4] = {s.x, s.y, s.z, s.w};
+        if constexpr (sizeof(TO) == 2) {
+            uint2 q;
+            q.x = (uint32_t)f32_to_bf16(w[0]) | ((uint32_t)f32_to_bf16(w[1]) << 16);
+            q.y = (uint32_t)f32_to_bf16(w[2]) | ((uint32_t)f32_to_bf16(w[3]) << 16);
+            *reinterpret_cast<uint2*>(dx + (size_t)t * H + c) = q;
+        } else {
+            *reinterpret_cast<float4*>(dx + (size_t)t * H + c) = make_float4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+template <typename TX>
+__device__ __forceinline__ float to_f32(TX v);
+template <>
+__device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+
+constexpr int kBankRows = 16;   // bank rows per workgroup
+constexpr int kBankT = 64;      // tokens staged per step
+
+// dbank[j][h] = sum over t (ascending) of dz[t][j] * x[t][h], fp32.
+// grid (ceil(H/256), ceil(NE/16)); thread h = 256*bx + tid.
+template <typename TX>
+__global__ __launch_bounds__(256) void dbank_kernel(const float* __restrict__ dz, const TX* __restrict__ x, int T,
+                                                    int H, int NE, float* __restrict__ dbank) {
+    __shared__ float zs[kBankT][kBankRows];
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    const int j0 = blockIdx.y * kBankRows;
+    float acc[kBankRows];
+#pragma unroll
+    for (int j = 0; j < kBankRows; ++j) acc[j] = 0.f;
+    for (int t0 = 0; t0 < T; t0 += kBankT) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < kBankT * kBankRows; i += 256) {
+            const int tt = t0 + i / kBankRows, j = j0 + i % kBankRows;
+            zs[i / kBankRows][i % kBankRows] = (tt < T && j < NE) ? dz[(size_t)tt * NE + j] : 0.f;
+        }
+        __syncthreads();
+        if (h < H) {
+            const int tn = min(kBankT, T - t0);
+            for (int tt = 0; tt < tn; ++tt) {
+                const float xv = to_f32<TX>(x[(size_t)(t0 + tt) * H + h]);
+#pragma unroll
+                for (int j = 0; j < kBankRows; ++j) acc[j] += zs[tt][j] * xv;
+            }
+        }
+    }
+    if (h < H) {
+#pragma unroll
+        for (int j = 0; j < kBankRows; ++j)
+            if (j0 + j < NE) dbank[(size_t)(j0 + j) * H + h] = acc[j];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather_transpose(int dtype, const void* src, void* out, const int32_t* map, int n_rows, int C,
+                                   int D, int batch, long long src_batch, long long out_batch, hipStream_t stream) {
+    if (C <= 0 || D <= 0 || batch <= 0) return hipSuccess;
+    dim3 grid((C + kTrTile - 1) / kTrTile, (D + kTrTile - 1) / kTrTile, batch);
+    if (dtype == 1)
+        hipLaunchKernelGGL(gather_transpose_kernel<bf16_t>, grid, dim3(256), 0, stream, (const bf16_t*)src,
+                           (bf16_t*)out, map, n_rows, C, D, src_batch, out_batch);
+    else
+        hipLaunchKernelGGL(gather_transpose_kernel<float>, grid, dim3(256), 0, stream, (const float*)src,
+                           (float*)out, map, n_rows, C, D, src_batch, out_batch);
+    return hipGetLastError();
+}
+
+hipError_t launch_column_map(const int32_t* counts, const int32_t* offsets, const int32_t* row_token, int E, int C,
+                             int32_t* poff, int32_t* col_row, int32_t* col_tok, hipStream_t stream) {
+    hipLaunchKernelGGL(padded_offsets_kernel, dim3(1), dim3(1024), 0, stream, counts, E, poff);
+    hipLaunchKernelGGL(column_map_kernel, dim3((C + 255) / 256), dim3(256), 0, stream, poff, offsets, row_token, E, C,
+                       col_row, col_tok);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_backward(const double* zpart, int ksplit, const int32_t* topk_idx, const int32_t* pos,
+                                  const float* dgp_r, const float* dgp_sh, int T, int E, int S, int k, int I,
+                                  float route_scale, float global_scale, float* dz, float* dzc, hipStream_t stream) {
+    const double scale = (double)route_scale * (double)global_scale;
+    hipLaunchKernelGGL(router_backward_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, zpart, ksplit, topk_idx, pos,
+                       dgp_r, dgp_sh, T, E, S, k, I, scale, dz, dzc);
+    return hipGetLastError();
+}
+
+hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, const int32_t* pos,
+                             const int32_t* topk_idx, const float* dzc, const float* bank, void* dx, int T, int H,
+                             int E, int S, int k, hipStream_t stream) {
+    const size_t items = (size_t)T * (H / 4);
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int blocks = (int)std::min<size_t>((items + 255) / 256, (size_t)std::max(cus, 1) * 16);
+    if (out_dtype == 1)
+        hipLaunchKernelGGL(dx_combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, dxr, dxs, pos, topk_idx, dzc,
+                           bank, (bf16_t*)dx, T, H, E, S, k);
+    else
+        hipLaunchKernelGGL(dx_combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, dxr, dxs, pos, topk_idx, dzc,
+                           bank, (float*)dx, T, H, E, S, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_dbank(int dtype, const float* dz, const void* x, int T, int H, int NE, float* dbank,
+                        hipStream_t stream) {
+    dim3 grid((H + 255) / 256, (NE + kBankRows - 1) / kBankRows);
+    if (dtype == 1)
+        hipLaunchKernelGGL(dbank_kernel<bf16_t>, grid, dim3(256), 0, stream, dz, (const bf16_t*)x, T, H, NE, dbank);
+    else
+        hipLaunchKernelGGL(dbank_kernel<float>, grid, dim3(256), 0, stream, dz, (const float*)x, T, H, NE, dbank);
+    return hipGetLastError();
+}
+
+}  // namespace inkling

@@ -41,8 +41,9 @@ constexpr int kWave = 64;
 
 // Tile descriptor of the routed grouped GEMMs: expert id and first row of the
 // tile within that expert's block of expert-sorted rows.
-// Per-XCD tile-round counters of the two grouped GEMM launches (8 each).
-constexpr int kRoundCounters = 16;
+// Per-XCD tile-round counters of the grouped GEMM launches (8 each: gate_up,
+// down, and the backward's dact).
+constexpr int kRoundCounters = 24;
 
 struct RoutedTile {
     int32_t expert;

@@ -31,7 +31,14 @@ namespace inkling {
 
 namespace {
 
-enum { kModeGateUp = 0, kModeDown = 1 };
+// kModeGateUp: SwiGLU * gamma epilogue -> activation rows (TE)
+// kModeDown: fp32 rows (routed rows go to their slot row)
+// kModeGateUpRaw: the gate_up projection itself -> h rows (fp32) (backward recompute)
+// kModeDAct: backward through down and SwiGLU: acc = dact; epilogue writes
+//            dh = d[gate, up] (TE), a = gamma * silu(g) * u (TE) and per-64-column
+//            partial sums of dact . silu(g) * u (the routing-weight gradient)
+// kModeWgrad: weight gradients, one problem per expert, K = that expert's rows
+enum { kModeGateUp = 0, kModeDown = 1, kModeGateUpRaw = 2, kModeDAct = 3, kModeWgrad = 4 };
 constexpr int kSpinLimit = 400;   // polls of a tile-round wait (about 100-400 us at most)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -58,6 +65,21 @@ struct GemmKArgs {
     int shared_blocks, shared_mtiles;
     int has_routed;
     int32_t* round_counter;    // [8]: tiles finished per XCD (zero at launch)
+    // kModeDAct
+    const void* h_routed;      // [T*k][2I] sorted rows, fp32
+    const void* h_shared;      // [T][S*2I] fp32
+    void* a_routed;            // [T*k][I] sorted rows
+    void* a_shared;            // [T][S*I]
+    float* dgp_routed;         // [T*k][I/64]
+    float* dgp_shared;         // [T][S*I/64]
+    // kModeWgrad: problems e < E (routed, K = padded rows of e at column
+    // offset poff[e]) then s < S (shared, K = K_s); out[m][n] = sum_k B[m][k] A[n][k]
+    const int32_t* poff;       // [E+1] padded column offsets
+    int ld_r, ld_s;            // row strides of the routed / shared operands
+    long long a_sh_stride, b_sh_stride;   // element offset of shared problem s in A / B
+    int wg_E, wg_M, wg_N, wg_mtiles, wg_ntiles;
+    float* w_out_routed;       // [E][M][N]
+    float* w_out_shared;       // [S][M][N]
 };
 
 template <typename TE>
@@ -102,6 +124,32 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
 template <>
 __device__ __forceinline__ void store4<float>(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename TE>
+__device__ __forceinline__ void load8f(const TE* p, float* v);
+template <>
+__device__ __forceinline__ void load8f<bf16_t>(const bf16_t* p, float* v) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(w[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load8f<float>(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename TE>
+__device__ __forceinline__ void store8(TE* p, const float* v) {
+    store4<TE>(p, v);
+    store4<TE>(p + 4, v + 4);
 }
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
@@ -149,16 +197,47 @@ template <typename TE>
 struct Tile {
     bool is_shared;
     int K, N, seg, n0, rows_valid, grow0, t0;
+    int lda, ldb;        // row strides of A and B (elements)
     const TE* A;
     const TE* B;
+    float* out;          // kModeWgrad: this problem's gradient [M][N]
 };
 
-template <typename TE, int BM, int GM>
+template <typename TE, int BM, int GM, int MODE>
 __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int BN) {
     Tile<TE> t;
-    t.is_shared = L < a.shared_blocks;
     t.grow0 = 0;
     t.t0 = 0;
+    t.out = nullptr;
+    if constexpr (MODE == kModeWgrad) {
+        const int per_p = a.wg_mtiles * a.wg_ntiles;
+        const int pr = L / per_p;
+        int mt, nt;
+        grouped<GM>(L - pr * per_p, a.wg_mtiles, a.wg_ntiles, mt, nt);
+        t.is_shared = pr >= a.wg_E;
+        t.t0 = mt * BM;
+        t.rows_valid = min(BM, a.wg_M - t.t0);
+        t.n0 = nt * BN;
+        t.N = a.wg_N;
+        if (!t.is_shared) {
+            const int k0 = a.poff[pr];
+            t.K = a.poff[pr + 1] - k0;
+            t.A = reinterpret_cast<const TE*>(a.A_routed) + k0;
+            t.B = reinterpret_cast<const TE*>(a.B_routed) + k0;
+            t.lda = t.ldb = a.ld_r;
+            t.out = a.w_out_routed + (size_t)pr * a.wg_M * a.wg_N;
+        } else {
+            const int sx = pr - a.wg_E;
+            t.K = a.K_s;
+            t.A = reinterpret_cast<const TE*>(a.A_shared) + sx * a.a_sh_stride;
+            t.B = reinterpret_cast<const TE*>(a.B_shared) + sx * a.b_sh_stride;
+            t.lda = t.ldb = a.ld_s;
+            t.out = a.w_out_shared + (size_t)sx * a.wg_M * a.wg_N;
+        }
+        t.seg = max(t.K, 1);
+        return t;
+    }
+    t.is_shared = L < a.shared_blocks;
     if (t.is_shared) {
         int mt, nt;
         grouped<GM>(L, a.shared_mtiles, a.ntn_s, mt, nt);
@@ -168,6 +247,8 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
         t.K = a.K_s;
         t.N = a.N_s;
         t.seg = a.seg_s;
+        t.lda = a.seg_s;
+        t.ldb = a.K_s;
         t.A = reinterpret_cast<const TE*>(a.A_shared);
         t.B = reinterpret_cast<const TE*>(a.B_shared);
     } else {
@@ -190,6 +271,8 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
         t.K = a.K_r;
         t.N = a.N_r;
         t.seg = a.K_r;
+        t.lda = a.K_r;
+        t.ldb = a.K_r;
         t.A = reinterpret_cast<const TE*>(a.A_routed) + (size_t)tl.expert * a.N_r * a.K_r;
         t.B = reinterpret_cast<const TE*>(a.B_routed);
     }
@@ -283,12 +366,15 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     // ---- this workgroup's tiles ---------------------------------------------
     // Each XCD takes a contiguous range of blocks holding an eighth of the K
     // stages (shared and routed blocks differ in K when S*I is concatenated).
-    const int nb_routed = a.has_routed ? (*a.num_tiles) * a.ntn_r : 0;
-    const int nb_real = a.shared_blocks + nb_routed;
+    // (weight gradients: one tile per workgroup, ranges by count)
+    const int nb_routed = MODE == kModeWgrad ? 0 : a.has_routed ? (*a.num_tiles) * a.ntn_r : 0;
+    const int nb_real = MODE == kModeWgrad ? (a.wg_E + a.S) * a.wg_mtiles * a.wg_ntiles
+                                           : a.shared_blocks + nb_routed;
     const long long cost_s = (long long)a.shared_blocks * a.K_s;
     const long long cost_all = cost_s + (long long)nb_routed * a.K_r;
     auto range_start = [&](int x) -> int {
         if (x >= 8) return nb_real;
+        if constexpr (MODE == kModeWgrad) return (int)((long long)nb_real * x / 8);
         const long long c = cost_all * x / 8;
         if (c <= 0) return 0;                                   // also K_s == 0 (no shared blocks)
         if (c <= cost_s) return (int)((c + a.K_s - 1) / a.K_s);
@@ -315,17 +401,18 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 #pragma unroll
         for (int q = 0; q < A_PW; ++q) {
             const int r = RPL * (wv + NW * q) + lr;
-            a_src[q] = t.A + (size_t)min(t.n0 + r, t.N - 1) * t.seg + (lp ^ sw(r)) * EPC;   // rows past N re-read N-1
+            a_src[q] = t.A + (size_t)min(t.n0 + r, t.N - 1) * t.lda + (lp ^ sw(r)) * EPC;   // rows past N re-read N-1
         }
 #pragma unroll
         for (int q = 0; q < B_PW; ++q) {
             const int r = RPL * (wv + NW * q) + lr;
             const int rr = min(r, t.rows_valid - 1);   // rows past the end re-read the last valid row
             size_t row;
-            if (t.is_shared) row = (size_t)(t.t0 + rr);
-            else if (MODE == kModeGateUp) row = (size_t)a.row_token[t.grow0 + rr];
+            if (t.is_shared || MODE == kModeWgrad) row = (size_t)(t.t0 + rr);
+            else if (MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct)
+                row = (size_t)a.row_token[t.grow0 + rr];   // routed token rows, gathered
             else row = (size_t)(t.grow0 + rr);
-            b_src[q] = t.B + row * t.K + (lp ^ sw(r)) * EPC;
+            b_src[q] = t.B + row * t.ldb + (lp ^ sw(r)) * EPC;
         }
         a_k = 0;
         b_k = 0;
@@ -380,13 +467,16 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     int ep_row[FM];               // down: output row (slot for routed tiles, token for shared tiles)
     int ep_s0 = 0;                // gate_up shared: expert of the wave's first weight row
     auto prefetch_epilogue = [&](const Tile<TE>& t) __attribute__((always_inline)) {
-        const int s0 = min((t.n0 + wn0) / (2 * a.I), max(a.S - 1, 0));
-        const int s1 = min((t.n0 + wn0 + WTN - 1) / (2 * a.I), max(a.S - 1, 0));
+        if constexpr (MODE == kModeGateUpRaw || MODE == kModeWgrad) return;
+        // columns of shared expert s: [s*2I, (s+1)*2I) in gate_up, [s*I, (s+1)*I) in dact
+        const int width = MODE == kModeDAct ? a.I : 2 * a.I;
+        const int s0 = min((t.n0 + wn0) / width, max(a.S - 1, 0));
+        const int s1 = min((t.n0 + wn0 + WTN - 1) / width, max(a.S - 1, 0));
         ep_s0 = s0;
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int m = min(16 * (WM * j + wm) + rl, t.rows_valid - 1);
-            if (MODE == kModeGateUp) {
+            if (MODE == kModeGateUp || MODE == kModeDAct) {
                 if (t.is_shared) {
                     ep_g0[j] = a.shared_g[(size_t)(t.t0 + m) * a.S + s0];
                     ep_g1[j] = a.shared_g[(size_t)(t.t0 + m) * a.S + s1];
@@ -511,7 +601,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         }
     };
 
-    Tile<TE> cur = decode_tile<TE, BM, GM>(a, L, BN);
+    Tile<TE> cur = decode_tile<TE, BM, GM, MODE>(a, L, BN);
     setup(cur);
     issue_first(cur.K / BK);
     prefetch_epilogue(cur);
@@ -561,7 +651,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         barrier_keep_loads();
         Tile<TE> nxt = cur;
         if (has_next) {
-            nxt = decode_tile<TE, BM, GM>(a, L, BN);
+            nxt = decode_tile<TE, BM, GM, MODE>(a, L, BN);
             setup(nxt);
             issue_first(nxt.K / BK);
         }
@@ -569,8 +659,60 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         // ---- epilogue of the current tile ----------------------------------
         // acc[i][j][r]: output column n = n0 + wn0 + 16i + 4*(lane/16) + r,
         // token row m = 16*(WM*j + wm) + lane%16
+        if constexpr (MODE == kModeDAct) {
+            // acc = dact (d of the activation the down projection saw); with
+            // h = [g, u] interleaved, p = silu(g) u, a = gamma p:
+            //   dgamma += dact . p,  dp = gamma dact,
+            //   dg = dp u silu'(g),  du = dp silu(g)
+            const int nrow = cur.N;   // I (routed) or S*I (shared) columns
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int m = 16 * (WM * j + wm) + rl;
+                const bool rv = j < nvb && m < cur.rows_valid && nvi > 0;
+                const size_t row = cur.is_shared ? (size_t)(cur.t0 + m) : (size_t)(cur.grow0 + m);
+                const float* hrow = reinterpret_cast<const float*>(cur.is_shared ? a.h_shared : a.h_routed) + row * 2 * nrow;
+                TE* dhrow = reinterpret_cast<TE*>(cur.is_shared ? a.out_shared : a.out_routed) + row * 2 * nrow;
+                TE* arow = reinterpret_cast<TE*>(cur.is_shared ? a.a_shared : a.a_routed) + row * nrow;
+                float part = 0.f;
+                if (rv) {
+#pragma unroll
+                    for (int i = 0; i < FN; ++i) {
+                        const int n = cur.n0 + wn0 + 16 * i + 4 * (lane >> 4);
+                        if (i < nvi) {
+                            const float g_ = (cur.is_shared && n / a.I != ep_s0) ? ep_g1[j] : ep_g0[j];
+                            float hv[8];
+                            load8f<float>(hrow + 2 * n, hv);
+                            float dh[8], av[4];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float gg = hv[2 * r], uu = hv[2 * r + 1];
+                                const float sg = 1.0f / (1.0f + __expf(-gg));
+                                const float si = gg * sg;
+                                const float pp = si * uu;
+                                const float da = acc[i][j][r];
+                                const float dp = g_ * da;
+                                part += da * pp;
+                                av[r] = g_ * pp;
+                                dh[2 * r] = dp * uu * sg * (1.0f + gg * (1.0f - sg));
+                                dh[2 * r + 1] = dp * si;
+                            }
+                            store8<TE>(dhrow + 2 * n, dh);
+                            store4<TE>(arow + n, av);
+                        }
+                    }
+                }
+                // row sum over the wave's 64 columns (lanes l, l^16, l^32, l^48 share the row)
+                part += __shfl_xor(part, 16);
+                part += __shfl_xor(part, 32);
+                if (rv && (lane >> 4) == 0) {
+                    float* dgp = cur.is_shared ? a.dgp_shared : a.dgp_routed;
+                    dgp[row * (nrow / 64) + (cur.n0 + wn0) / 64] = part;
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
+            if constexpr (MODE == kModeDAct) break;
             const int m = 16 * (WM * j + wm) + rl;
             if (j < nvb && m < cur.rows_valid) {
 #pragma unroll
@@ -578,7 +720,15 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
                     const int n = cur.n0 + wn0 + 16 * i + 4 * (lane >> 4);
                     if (i < nvi) {
                         const f32x4_t v = acc[i][j];
-                        if (MODE == kModeGateUp) {
+                        if (MODE == kModeGateUpRaw) {   // h kept in fp32 (not an MFMA operand)
+                            float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) +
+                                       (size_t)(cur.is_shared ? cur.t0 + m : cur.grow0 + m) * cur.N + n;
+                            float w[4] = {v[0], v[1], v[2], v[3]};
+                            store4<float>(o, w);
+                        } else if (MODE == kModeWgrad) {
+                            float w[4] = {v[0], v[1], v[2], v[3]};
+                            store4<float>(cur.out + (size_t)(cur.t0 + m) * cur.N + n, w);
+                        } else if (MODE == kModeGateUp) {
                             if (cur.is_shared) {
                                 const int t = cur.t0 + m;
                                 const float g = (n / (2 * a.I) == ep_s0) ? ep_g0[j] : ep_g1[j];
@@ -677,14 +827,16 @@ int num_cus() {
 template <typename TE, int MODE>
 hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t stream) {
     if (max_tiles <= 0) return hipSuccess;
-    // persistent: at most one workgroup per CU (LDS), a multiple of the 8 XCDs
-    int grid = std::min(max_tiles, num_cus() * (cfg == 0 ? 1 : kDecodeGridPerCU));
+    // persistent: at most one workgroup per CU (LDS), a multiple of the 8 XCDs;
+    // weight gradients (tiles of very different K) take one tile per workgroup
+    int grid = MODE == kModeWgrad ? max_tiles : std::min(max_tiles, num_cus() * (cfg == 0 ? 1 : kDecodeGridPerCU));
     grid = (grid + 7) / 8 * 8;
-    if (cfg == 0)
+    constexpr int kSync = MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kPrefillSyncGateUp
+                          : MODE == kModeDown ? kPrefillSyncDown : 0;
+    if (cfg == 0 || MODE == kModeWgrad)
         hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB, kPrefillRowB, 4,
-                                           MODE == kModeGateUp ? kPrefillSyncGateUp : kPrefillSyncDown, MODE>), dim3(grid),
-                           dim3(512), 0, stream, a);
-    else
+                                           kSync, MODE>), dim3(grid), dim3(512), 0, stream, a);
+    else if constexpr (MODE != kModeWgrad)
         hipLaunchKernelGGL((moe_gemm_kernel<TE, kDecodeBN, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, 0, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     return hipGetLastError();
@@ -790,6 +942,87 @@ hipError_t launch_dense_prep(float* gamma, int T, float value, int32_t* round_co
     const int blocks = std::max(1, (T + 255) / 256);
     hipLaunchKernelGGL(dense_prep_kernel, dim3(blocks), dim3(256), 0, stream, gamma, T, value, round_counters);
     return hipGetLastError();
+}
+
+// ---- backward ---------------------------------------------------------------
+
+hipError_t launch_gate_up_raw(const MoeGemmParams& p, void* h_r, void* h_sh, hipStream_t stream) {
+    GemmKArgs a = base_args(p);
+    const int bm = gemm_cfg_bm(p.cfg);
+    a.A_routed = p.w_gu;
+    a.B_routed = p.x;
+    a.out_routed = h_r;
+    a.K_r = p.H;
+    a.N_r = 2 * p.I;
+    a.ntn_r = (a.N_r + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
+    a.has_routed = p.has_routed;
+    a.A_shared = p.wsh_gu;
+    a.B_shared = p.x;
+    a.out_shared = h_sh;
+    a.K_s = p.H;
+    a.N_s = 2 * p.I * p.S;
+    a.ntn_s = (a.N_s + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
+    a.seg_s = p.H;
+    a.shared_mtiles = (p.T + bm - 1) / bm;
+    a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
+    return launch_dispatch<kModeGateUpRaw>(p, a, a.shared_blocks + (p.has_routed ? p.max_routed_tiles * a.ntn_r : 0),
+                                           stream);
+}
+
+hipError_t launch_dact(const MoeGemmParams& p, const BwdActBufs& b, hipStream_t stream) {
+    GemmKArgs a = base_args(p);
+    const int bm = gemm_cfg_bm(p.cfg);
+    a.round_counter = p.round_counters + 16;
+    a.A_routed = b.wdT;        // [E][I][H]
+    a.B_routed = b.dout;       // token rows gathered
+    a.out_routed = b.dh_r;
+    a.K_r = p.H;
+    a.N_r = p.I;
+    a.ntn_r = (a.N_r + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
+    a.has_routed = p.has_routed;
+    a.A_shared = b.wshdT;      // [S*I][H]
+    a.B_shared = b.dout;
+    a.out_shared = b.dh_sh;
+    a.K_s = p.H;
+    a.N_s = p.I * p.S;
+    a.ntn_s = (a.N_s + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
+    a.seg_s = p.H;
+    a.shared_mtiles = (p.T + bm - 1) / bm;
+    a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
+    a.h_routed = b.h_r;
+    a.h_shared = b.h_sh;
+    a.a_routed = b.a_r;
+    a.a_shared = b.a_sh;
+    a.dgp_routed = b.dgp_r;
+    a.dgp_shared = b.dgp_sh;
+    return launch_dispatch<kModeDAct>(p, a, a.shared_blocks + (p.has_routed ? p.max_routed_tiles * a.ntn_r : 0),
+                                      stream);
+}
+
+hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream) {
+    GemmKArgs a = {};
+    a.A_routed = w.A_r;
+    a.B_routed = w.B_r;
+    a.A_shared = w.A_s;
+    a.B_shared = w.B_s;
+    a.poff = w.poff;
+    a.ld_r = w.ld_r;
+    a.ld_s = w.ld_s;
+    a.K_s = w.K_s;
+    a.K_r = 1;
+    a.a_sh_stride = w.a_sh_stride;
+    a.b_sh_stride = w.b_sh_stride;
+    a.S = w.S;
+    a.wg_E = w.E;
+    a.wg_M = w.M;
+    a.wg_N = w.N;
+    a.wg_mtiles = (w.M + 255) / 256;
+    a.wg_ntiles = (w.N + kPrefillBN - 1) / kPrefillBN;
+    a.w_out_routed = w.out_r;
+    a.w_out_shared = w.out_s;
+    const int tiles = (w.E + w.S) * a.wg_mtiles * a.wg_ntiles;
+    if (w.dtype == 1) return launch_mode<bf16_t, kModeWgrad>(0, a, tiles, stream);
+    return launch_mode<float, kModeWgrad>(0, a, tiles, stream);
 }
 
 }  // namespace inkling

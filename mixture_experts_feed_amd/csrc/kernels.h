@@ -65,6 +65,58 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
 // routed (act_r -> y) and shared (act_sh -> ysh) down projections, one launch
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream);
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream);
+// ---- backward GEMMs (gemm.hip) ---------------------------------------------
+// h = gate_up(x) (no SwiGLU, fp32) for routed rows [T*k][2I] and shared [T][S*2I]
+hipError_t launch_gate_up_raw(const MoeGemmParams& p, void* h_r, void* h_sh, hipStream_t stream);
+struct BwdActBufs {
+    const void* wdT;     // [E][I][H] routed down projections, transposed
+    const void* wshdT;   // [S*I][H]  shared down projections, transposed
+    const void* dout;    // [T][H]
+    const void* h_r;     // [T*k][2I] fp32
+    const void* h_sh;    // [T][S*2I] fp32
+    void* dh_r;          // [T*k][2I]
+    void* dh_sh;         // [T][S*2I]
+    void* a_r;           // [T*k][I]
+    void* a_sh;          // [T][S*I]
+    float* dgp_r;        // [T*k][I/64]
+    float* dgp_sh;       // [T][S*I/64]
+};
+// dact = down^T dout per routed row / shared token, then the SwiGLU backward:
+// dh, a and partial routing-weight gradients (round counters 16..23)
+hipError_t launch_dact(const MoeGemmParams& p, const BwdActBufs& b, hipStream_t stream);
+// out_p[m][n] = sum_k B_p[m][k] A_p[n][k] for problems p < E (routed: K and
+// the column offset from poff) and S shared ones (K = K_s)
+struct WgradParams {
+    int dtype, E, S, M, N;
+    const void* A_r;
+    const void* B_r;
+    const void* A_s;
+    const void* B_s;
+    const int32_t* poff;
+    int ld_r, ld_s, K_s;
+    long long a_sh_stride, b_sh_stride;
+    float* out_r;
+    float* out_s;
+};
+hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream);
+
+// ---- backward, other kernels (backward.hip) --------------------------------
+// out_b[d][c] = src_b[row(c)][d]; row(c) = map[c] (-1: zero) or c (< n_rows)
+hipError_t launch_gather_transpose(int dtype, const void* src, void* out, const int32_t* map, int n_rows, int C,
+                                   int D, int batch, long long src_batch, long long out_batch, hipStream_t stream);
+// poff [E+1]: experts' row counts rounded up to 64, prefix-summed; for padded
+// columns c < C the sorted row (or -1) and its token (or -1)
+hipError_t launch_column_map(const int32_t* counts, const int32_t* offsets, const int32_t* row_token, int E, int C,
+                             int32_t* poff, int32_t* col_row, int32_t* col_tok, hipStream_t stream);
+hipError_t launch_router_backward(const double* zpart, int ksplit, const int32_t* topk_idx, const int32_t* pos,
+                                  const float* dgp_r, const float* dgp_sh, int T, int E, int S, int k, int I,
+                                  float route_scale, float global_scale, float* dz, float* dzc, hipStream_t stream);
+hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, const int32_t* pos,
+                             const int32_t* topk_idx, const float* dzc, const float* bank, void* dx, int T, int H,
+                             int E, int S, int k, hipStream_t stream);
+hipError_t launch_dbank(int dtype, const float* dz, const void* x, int T, int H, int NE, float* dbank,
+                        hipStream_t stream);
+
 // gamma[t] = value for t < T; the GEMM round counters zeroed (the dense MLP's
 // stand-in for the router and the permutation)
 hipError_t launch_dense_prep(float* gamma, int T, float value, int32_t* round_counters, hipStream_t stream);

@@ -278,10 +278,12 @@ def silu_grad(v) -> np.ndarray:
     return s * (1.0 + v * (1.0 - s))
 
 
-def expert_backward(rows, w_gu, w_d, gammas, dout_rows):
+def expert_backward(rows, w_gu, w_d, gammas, dout_rows, with_abs=False):
     """Backward of gamma * down(swiglu(gate_up(rows))) for the rows one expert
     received.  Returns (d rows [n, H], d gate_up [2I, H], d down [H, I],
-    d gammas [n])."""
+    d gammas [n]); with_abs adds the sums of absolute products of the two
+    weight-gradient contractions, |dh|^T |rows| and |dout|^T |a| (the scale of
+    the componentwise rounding-error bound of those sums)."""
     X, Wgu, Wd, G = _f64(rows), _f64(w_gu), _f64(w_d), _f64(dout_rows)
     gam = _f64(gammas)
     h = X @ Wgu.T
@@ -295,6 +297,8 @@ def expert_backward(rows, w_gu, w_d, gammas, dout_rows):
     dh = np.empty_like(h)
     dh[:, 0::2] = dp * u * silu_grad(g)
     dh[:, 1::2] = dp * silu(g)
+    if with_abs:
+        return dh @ Wgu, dh.T @ X, d_wd, d_gam, np.abs(dh).T @ np.abs(X), np.abs(G).T @ np.abs(a)
     return dh @ Wgu, dh.T @ X, d_wd, d_gam
 
 
@@ -323,7 +327,8 @@ def router_backward(z, bias, n_routed: int, topk_indices, topk_weights, shared_g
 
 
 def moe_backward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int, route_scale: float,
-                 global_scale: float, dout, padding_mask=None, routing=None, tokens=None, experts=None):
+                 global_scale: float, dout, padding_mask=None, routing=None, tokens=None, experts=None,
+                 with_abs=False):
     """Gradients of L = sum(dout * InklingMoE.forward(x)) in fp64.
 
     Returns a dict:
@@ -331,7 +336,9 @@ def moe_backward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int, route
       d_w_gu {e: [2I, H]}, d_w_d {e: [H, I]} for the routed experts in
       `experts` (default all; an expert that received no token has zero
       gradients); d_wsh_gu [S, 2I, H], d_wsh_d [S, H, I]; dz [T', E+S];
-      d_topk_weights [T', k], d_shared_gammas [T', S].
+      d_topk_weights [T', k], d_shared_gammas [T', S];
+      with_abs: abs_w_gu / abs_w_d (dicts like d_w_gu / d_w_d) and abs_wsh_gu /
+      abs_wsh_d, the sums of absolute products of each weight gradient.
     Padded tokens skip the routed experts (their routed weights get no
     gradient) and keep the shared experts."""
     x, G = _f64(x), _f64(dout)
@@ -350,44 +357,53 @@ def moe_backward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int, route
     dx = np.zeros((R, H), dtype=F64)
     d_tw = np.zeros((R, top_k), dtype=F64)
     d_sg = np.zeros((R, S), dtype=F64)
-    res = {"d_w_gu": {}, "d_w_d": {}}
+    res = {"d_w_gu": {}, "d_w_d": {}, "abs_w_gu": {}, "abs_w_d": {}}
     # routed experts: pairs (local row, choice) of the rows asked for
     lt_all, li_all = np.nonzero(~pad[rows][:, None] & (ti[rows] >= 0))
     e_all = ti[rows][lt_all, li_all]
     for e in np.unique(e_all):
         m = e_all == e
         lt, li = lt_all[m], li_all[m]
-        dX, dgu, dd, dgam = expert_backward(x[rows][lt], w_gu[e], w_d[e], tw[rows][lt, li], G[rows][lt])
+        out = expert_backward(x[rows][lt], w_gu[e], w_d[e], tw[rows][lt, li], G[rows][lt],
+                              with_abs=with_abs and tokens is None)
+        dX, dgu, dd, dgam = out[:4]
         np.add.at(dx, lt, dX)
         d_tw[lt, li] = dgam
         if tokens is None:
             res["d_w_gu"][int(e)], res["d_w_d"][int(e)] = dgu, dd
+            if with_abs:
+                res["abs_w_gu"][int(e)], res["abs_w_d"][int(e)] = out[4], out[5]
     # weight gradients of the asked experts over every token (when rows was a subset)
     for e in want:
         if e in res["d_w_gu"]:
             continue
         t_e, i_e = np.nonzero(~pad[:, None] & (ti == e))
         if len(t_e) == 0:
-            res["d_w_gu"][e] = np.zeros_like(_f64(w_gu[e]))
-            res["d_w_d"][e] = np.zeros_like(_f64(w_d[e]))
+            res["d_w_gu"][e] = res["abs_w_gu"][e] = np.zeros_like(_f64(w_gu[e]))
+            res["d_w_d"][e] = res["abs_w_d"][e] = np.zeros_like(_f64(w_d[e]))
             continue
-        _, dgu, dd, _ = expert_backward(x[t_e], w_gu[e], w_d[e], tw[t_e, i_e], G[t_e])
-        res["d_w_gu"][e], res["d_w_d"][e] = dgu, dd
+        out = expert_backward(x[t_e], w_gu[e], w_d[e], tw[t_e, i_e], G[t_e], with_abs=with_abs)
+        res["d_w_gu"][e], res["d_w_d"][e] = out[1], out[2]
+        if with_abs:
+            res["abs_w_gu"][e], res["abs_w_d"][e] = out[4], out[5]
     if experts is not None:
-        res["d_w_gu"] = {e: res["d_w_gu"][e] for e in want}
-        res["d_w_d"] = {e: res["d_w_d"][e] for e in want}
+        for name in ("d_w_gu", "d_w_d", "abs_w_gu", "abs_w_d"):
+            res[name] = {e: res[name][e] for e in want if e in res[name]}
     # shared experts: every token
-    d_wsh_gu, d_wsh_d = [], []
+    d_wsh_gu, d_wsh_d, abs_wsh_gu, abs_wsh_d = [], [], [], []
     for s in range(S):
+        full = expert_backward(x, wsh_gu[s], wsh_d[s], sg[:, s], G, with_abs=with_abs)
         if tokens is None:
-            dX, dgu, dd, dgam = expert_backward(x, wsh_gu[s], wsh_d[s], sg[:, s], G)
+            dX, dgam = full[0], full[3]
         else:
             dX, _, _, dgam = expert_backward(x[rows], wsh_gu[s], wsh_d[s], sg[rows, s], G[rows])
-            _, dgu, dd, _ = expert_backward(x, wsh_gu[s], wsh_d[s], sg[:, s], G)
         dx += dX
         d_sg[:, s] = dgam
-        d_wsh_gu.append(dgu)
-        d_wsh_d.append(dd)
+        d_wsh_gu.append(full[1])
+        d_wsh_d.append(full[2])
+        if with_abs:
+            abs_wsh_gu.append(full[4])
+            abs_wsh_d.append(full[5])
     # router
     dz = router_backward(z[rows], bias, E, ti[rows], tw[rows], sg[rows], d_tw, d_sg, route_scale, global_scale)
     dx += dz @ _f64(gate_bank)
@@ -395,4 +411,7 @@ def moe_backward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int, route
                d_wsh_gu=np.array(d_wsh_gu).reshape((S,) + np.shape(_f64(wsh_gu[0])) if S else (0,)),
                d_wsh_d=np.array(d_wsh_d).reshape((S,) + np.shape(_f64(wsh_d[0])) if S else (0,)))
     res["d_gate_bank"] = dz.T @ x if tokens is None else None
+    if with_abs:
+        res["abs_wsh_gu"] = np.array(abs_wsh_gu).reshape(res["d_wsh_gu"].shape)
+        res["abs_wsh_d"] = np.array(abs_wsh_d).reshape(res["d_wsh_d"].shape)
     return res

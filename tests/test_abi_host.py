@@ -173,3 +173,28 @@ def test_dense_pointer_and_workspace_checks(lib):
     assert f(ctypes.byref(dims), x, w, w, 1.0, out, ws, n.value - 1, None) == B.INKLING_ERR_WORKSPACE
     zero = B.DenseDims(0, 128, 256, B.INKLING_BF16, B.INKLING_BF16)
     assert f(ctypes.byref(zero), None, None, None, 1.0, None, None, 0, None) == B.INKLING_OK
+
+
+def test_backward_argument_checks(lib):
+    d = _dims()
+    n = ctypes.c_size_t(0)
+    assert lib.inkling_moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.INKLING_OK
+    nf = ctypes.c_size_t(0)
+    lib.inkling_moe_workspace_size(ctypes.byref(d), ctypes.byref(nf))
+    assert n.value > nf.value
+    gate = B.Gate(0x1000, 0x1000, 1.0, 1.0)
+    ex = B.Experts(0x1000, 0x1000, 0x1000, 0x1000)
+    gr = B.Grads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    x, dout, dx, ws = (ctypes.c_void_p(v) for v in (0x4000, 0x5000, 0x6000, 0x7000))
+    bw = lib.inkling_moe_backward
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, None, dx, ctypes.byref(gr), ws,
+              n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, dout, ctypes.byref(gr), ws,
+              n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
+    no_sh = B.Grads(0x1000, 0x1000, 0x1000, None, None)
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, dx, ctypes.byref(no_sh), ws,
+              n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, dx, ctypes.byref(gr), ws,
+              n.value - 1, None) == B.INKLING_ERR_WORKSPACE
+    bad = _dims(hidden=96)
+    assert lib.inkling_moe_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == B.INKLING_ERR_UNSUPPORTED

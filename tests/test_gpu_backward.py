@@ -1,0 +1,160 @@
+"""GPU parity of inkling_moe_backward against the fp64 oracle's backward.
+
+Every gradient (dx, gate bank, routed and shared gate_up / down weights) is
+compared element by element on small workloads; at hidden=6144 the gradients
+of sampled tokens and of sampled experts are compared.
+
+Bars.  fp32 operands: max |gpu - oracle| <= 1e-4 * RMS(oracle) for every
+gradient.  bf16 operands: dx and the gate-bank gradient, max |gpu - oracle| <=
+2e-2 * RMS (the forward's bar); the weight gradients are sums over rows of
+products u_r v_r of which one factor (dh for gate_up, a = gamma * silu(g) * u for
+down) is rounded to bf16 to feed the bf16 matrix cores (unit roundoff 2^-8:
+8 significand bits), the other an exact bf16 input, with fp32 accumulation; so
+each element obeys the componentwise bound |err| <= (2^-8 + K 2^-24) sum_r |u_r v_r|,
+at most (2^-8 + 2^-10) sum_r |u_r v_r| for K <= 16384 rows; the oracle returns
+those sums.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_feed_amd import binding as B
+from mixture_experts_feed_amd import workloads as wl
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+ABS_BOUND = 2.0 ** -8 + 2.0 ** -10
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _dout(w, seed=7):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((w.T, w.hidden), generator=g).to(w.torch_dtype).to(DEV)
+
+
+def _close(name, gpu, ref, dtype, report=None):
+    g = gpu.float().cpu().numpy().astype(np.float64) if isinstance(gpu, torch.Tensor) else gpu
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(g - ref))) if ref.size else 0.0
+    rel = err / rms if rms > 0 else 0.0
+    _say(f"[backward]   {name}: max_err/rms={rel:.2e}")
+    assert err <= TOL[dtype] * rms + 1e-30, f"{name}: max abs err {err:.3e} > {TOL[dtype]} * RMS {rms:.3e}"
+    return rel
+
+
+def _close_wgrad(name, gpu, ref, absref, dtype):
+    """Weight gradients: the componentwise bound for bf16, the RMS bar for fp32."""
+    if dtype == "f32":
+        return _close(name, gpu, ref, dtype)
+    g = gpu.float().cpu().numpy().astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    excess = np.abs(g - ref) - ABS_BOUND * np.asarray(absref) - 1e-6 * rms
+    worst = float(np.max(np.abs(g - ref) / (np.asarray(absref) + 1e-30 * rms + 1e-300)))
+    _say(f"[backward]   {name}: max |err| / sum|u v| = {worst:.2e} (bound {ABS_BOUND:.2e}), "
+         f"max_err/rms={float(np.max(np.abs(g - ref))) / rms:.2e}")
+    assert np.all(excess <= 0), f"{name}: {int(np.sum(excess > 0))} elements above the bound"
+    return worst
+
+
+def _run(w, inp, dout, padding_mask=None):
+    S = w.n_shared
+    out = B.backward(inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"],
+                     inp["wsh_gu"] if S else None, inp["wsh_d"] if S else None, w.top_k, inp["route_scale"],
+                     inp["global_scale"], dout, padding_mask=padding_mask, dx_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return out
+
+
+def _full_backward(w, padding_mask=None):
+    _say(f"[backward] {w}")
+    inp = wl.make_inputs(w, device=DEV)
+    dout = _dout(w)
+    g = _run(w, inp, dout, padding_mask)
+    S = w.n_shared
+    pm = None if padding_mask is None else padding_mask.cpu().numpy().astype(bool)
+    ref = oracle.moe_backward(P.host(inp["x"]), P.host(inp["gate_bank"]), P.host(inp["bias"]),
+                              P.HostExperts(inp["w_gu"]), P.HostExperts(inp["w_d"]),
+                              P.HostExperts(inp["wsh_gu"] if S else None), P.HostExperts(inp["wsh_d"] if S else None),
+                              w.top_k, w.route_scale, w.global_scale, P.host(dout), padding_mask=pm, with_abs=True)
+    E = w.n_routed
+    st = lambda d: np.stack([d[e] for e in range(E)])
+    rel = {"dx": _close("dx", g["dx"], ref["dx"], w.dtype),
+           "d_gate_bank": _close("d_gate_bank", g["d_gate_bank"], ref["d_gate_bank"], w.dtype),
+           "d_w_gu": _close_wgrad("d_w_gu", g["d_w_gu"], st(ref["d_w_gu"]), st(ref["abs_w_gu"]), w.dtype),
+           "d_w_d": _close_wgrad("d_w_d", g["d_w_d"], st(ref["d_w_d"]), st(ref["abs_w_d"]), w.dtype)}
+    if S:
+        rel["d_wsh_gu"] = _close_wgrad("d_wsh_gu", g["d_wsh_gu"], ref["d_wsh_gu"], ref["abs_wsh_gu"], w.dtype)
+        rel["d_wsh_d"] = _close_wgrad("d_wsh_d", g["d_wsh_d"], ref["d_wsh_d"], ref["abs_wsh_d"], w.dtype)
+    _say("[backward] ok: " + " ".join(f"{k}={v:.2e}" for k, v in rel.items()))
+    return g
+
+
+CASES = {
+    "tiny_fp32": wl.WORKLOADS["tiny_fp32"],
+    "ragged_bf16": wl.custom(T=200, hidden=256, n_routed=16, top_k=4, n_shared=2, intermediate=128,
+                             route_scale=2.5, gate_dist=("uniform", 0.05), bias_dist=("uniform", 0.05)),
+    "few_rows_empty_experts": wl.custom(T=37, hidden=256, n_routed=32, top_k=3, n_shared=1, intermediate=192),
+    "no_shared": wl.custom(T=100, hidden=128, n_routed=8, top_k=2, n_shared=0, intermediate=64),
+    "f32_many_rows": wl.custom(T=300, hidden=128, n_routed=4, top_k=2, n_shared=1, intermediate=64, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward(name):
+    _full_backward(CASES[name])
+
+
+def test_backward_padding_mask():
+    w = CASES["ragged_bf16"]
+    g = torch.Generator().manual_seed(11)
+    mask = (torch.rand((w.T,), generator=g) < 0.3).to(torch.uint8).to(DEV)
+    _full_backward(w, padding_mask=mask)
+
+
+def test_backward_small_bf16():
+    _full_backward(wl.WORKLOADS["small_bf16"])
+
+
+def test_backward_deterministic():
+    w = CASES["ragged_bf16"]
+    inp = wl.make_inputs(w, device=DEV)
+    dout = _dout(w)
+    a = _run(w, inp, dout)
+    b = _run(w, inp, dout)
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+
+
+def test_backward_prefill_h6144_sampled():
+    """hidden=6144, T=8192: dx of sampled tokens, the weight gradients of two
+    routed experts and of the shared experts, against the oracle."""
+    w = wl.WORKLOADS["prefill_h6144"]
+    inp = wl.make_inputs(w, device=DEV)
+    dout = _dout(w)
+    g = _run(w, inp, dout)
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, w.T - 1] + rng.choice(w.T, size=10, replace=False).tolist()))
+    experts = [3, 77]
+    ref = oracle.moe_backward(P.host(inp["x"]), P.host(inp["gate_bank"]), P.host(inp["bias"]),
+                              P.HostExperts(inp["w_gu"]), P.HostExperts(inp["w_d"]), P.HostExperts(inp["wsh_gu"]),
+                              P.HostExperts(inp["wsh_d"]), w.top_k, w.route_scale, w.global_scale, P.host(dout),
+                              tokens=rows, experts=experts, with_abs=True)
+    rel = {"dx": _close("dx", g["dx"][rows], ref["dx"], "bf16")}
+    for e in experts:
+        rel[f"d_w_gu[{e}]"] = _close_wgrad("d_w_gu", g["d_w_gu"][e], ref["d_w_gu"][e], ref["abs_w_gu"][e], "bf16")
+        rel[f"d_w_d[{e}]"] = _close_wgrad("d_w_d", g["d_w_d"][e], ref["d_w_d"][e], ref["abs_w_d"][e], "bf16")
+    rel["d_wsh_gu"] = _close_wgrad("d_wsh_gu", g["d_wsh_gu"], ref["d_wsh_gu"], ref["abs_wsh_gu"], "bf16")
+    rel["d_wsh_d"] = _close_wgrad("d_wsh_d", g["d_wsh_d"], ref["d_wsh_d"], ref["abs_wsh_d"], "bf16")
+    _say("[backward] prefill_h6144 ok: " + " ".join(f"{k}={v:.2e}" for k, v in rel.items()))

@@ -465,3 +465,19 @@ def test_router_backward_weights_sum_rule():
     const = np.full((4, 2), 0.37)
     dz = oracle.router_backward(z, c["bias"], 5, ti, tw, sg, const, np.full((4, 2), 0.37), c["rs"], c["gs"])
     assert np.allclose(dz, 0.0, atol=1e-14)
+
+
+def test_backward_abs_sums_bound_the_gradients():
+    """The absolute-product sums returned for the tolerance bound are >= |grad|
+    elementwise, and equal to it for an expert that received a single row."""
+    c = _bw_case(37, T=5, E=4, k=2, S=1)
+    g = oracle.moe_backward(c["x"], c["bank"], c["bias"], c["w_gu"], c["w_d"], c["wsh_gu"], c["wsh_d"], c["k"],
+                            c["rs"], c["gs"], c["dout"], with_abs=True)
+    for e in g["d_w_gu"]:
+        assert np.all(g["abs_w_gu"][e] >= np.abs(g["d_w_gu"][e]) - 1e-14)
+        assert np.all(g["abs_w_d"][e] >= np.abs(g["d_w_d"][e]) - 1e-14)
+    assert np.all(g["abs_wsh_gu"] >= np.abs(g["d_wsh_gu"]) - 1e-14)
+    ti = oracle.route(oracle.gate_logits(c["x"], c["bank"]), c["bias"], 4, 2, c["rs"], c["gs"])[1]
+    single = [e for e in range(4) if np.sum(ti == e) == 1]
+    for e in single:
+        assert np.allclose(g["abs_w_gu"][e], np.abs(g["d_w_gu"][e]), rtol=1e-13, atol=1e-15)
