@@ -188,6 +188,7 @@ def main():
     ap.add_argument("--decode-workload", default="decode_h6144")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the InklingDenseMLP line")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -318,6 +319,35 @@ def main():
                                "frac_of_peak": round(dtf / PEAK_BF16_TFLOPS, 4), "flops_per_step": dw.flops_alg()}
         log(f"[bench] dense MLP {dms:.3f} ms, {dtf:.1f} TFLOP/s")
         del dn, dws, dout
+
+    if not args.no_backward:
+        # backward of the same prefill step: gradients of <dout, out>
+        bw_steps = max(3, args.steps // 4)
+        dout_b = torch.randn(inp["x"].shape, generator=torch.Generator().manual_seed(7)).to(inp["x"].dtype).to(dev)
+        bdims = B.make_dims(w.T, w.hidden, w.n_routed, w.top_k, S, w.intermediate, w.torch_dtype)
+        bws = torch.empty(B.backward_workspace_size(bdims), dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        grads = {"dx": torch.empty_like(inp["x"]), "d_gate_bank": torch.empty(tuple(inp["gate_bank"].shape), **f32),
+                 "d_w_gu": torch.empty(tuple(inp["w_gu"].shape), **f32), "d_w_d": torch.empty(tuple(inp["w_d"].shape), **f32),
+                 "d_wsh_gu": torch.empty(tuple(inp["wsh_gu"].shape), **f32),
+                 "d_wsh_d": torch.empty(tuple(inp["wsh_d"].shape), **f32)}
+
+        def bw_call():
+            B.backward(inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"], inp["wsh_gu"], inp["wsh_d"],
+                       w.top_k, w.route_scale, w.global_scale, dout_b, workspace=bws, grads=grads)
+
+        bms, _ = run_timed(torch, B, bw_call, bw_steps, 2, events)
+        # algorithmic: dact, dx, d down, d gate_up (12 T (k+S) H I) and the gate bank (2 T H (E+S));
+        # the gate_up recompute (4 T (k+S) H I) is reported beside it
+        bw_flops = 12.0 * w.T * (w.top_k + S) * w.hidden * w.intermediate + 2.0 * w.T * w.hidden * w.n_total
+        re_flops = 4.0 * w.T * (w.top_k + S) * w.hidden * w.intermediate
+        btf = bw_flops / (bms * 1e-3) / 1e12
+        result["backward"] = {"workload": w.name, "ms_per_step": round(bms, 4), "TFLOP_s": round(btf, 2),
+                              "frac_of_peak": round(btf / PEAK_BF16_TFLOPS, 4), "flops_alg": bw_flops,
+                              "recompute_flops": re_flops,
+                              "TFLOP_s_with_recompute": round((bw_flops + re_flops) / (bms * 1e-3) / 1e12, 2)}
+        log(f"[bench] backward {bms:.3f} ms, {btf:.1f} TFLOP/s algorithmic")
+        del bws, grads, dout_b
 
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_tokens} tokens")
