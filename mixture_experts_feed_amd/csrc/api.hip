@@ -148,7 +148,7 @@ struct BwdLayout {
     Layout F;   // the forward's routing and row buffers (y / ysh hold the dx rows)
     int Cmax, Tpad;
     size_t h_r, h_sh, dh_r, dh_sh, wdT, wshdT, wguT, wshguT, dgp_r, dgp_sh, dz, dzc, poff, col_row, col_tok;
-    size_t GsT, xsT, aT, dhT, GT, xT, a_shT, dh_shT, total;
+    size_t GsT, xsT, aT, dhT, GT, xT, a_shT, dh_shT, dbank_part, total;
 };
 
 BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
@@ -194,6 +194,7 @@ BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
     B.xT = take(H * Tp * es);
     B.a_shT = take(S * I * Tp * es);
     B.dh_shT = take(S * 2 * I * Tp * es);
+    B.dbank_part = take((size_t)dbank_partial_floats((int)H, (int)(E + S)) * 4);
     B.total = o;
     return B;
 }
@@ -514,7 +515,7 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
                               rb.pos, rb.topk_idx, dzc, gate->gate_bank, dx, T, H, E, S, k, s));
 
     // 6. gate bank gradient
-    HIP_TRY(launch_dbank(dt, dz, x, T, H, E + S, g->d_gate_bank, s));
+    HIP_TRY(launch_dbank(dt, dz, x, T, H, E + S, at<float>(workspace, B.dbank_part), g->d_gate_bank, s));
 
     // 7. weight gradients: operands transposed so that K (rows of an expert,
     //    each expert's columns padded to 64 with zeros; or tokens) is contiguous

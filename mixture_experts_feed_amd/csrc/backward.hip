@@ -25,29 +25,39 @@ constexpr int kTrTile = 64;
 
 // out_b[d][c] = src_b[row(c)][d] for d < D, c < C, with row(c) = map[c]
 // (map != NULL; -1 gives 0) or c (c < n_rows, else 0).  src rows have D
-// elements, out rows C.  64x64 tiles through LDS, 256 threads.
+// elements, out rows C; C and D are multiples of 64.  64x64 tiles through LDS,
+// 16-byte loads and stores on both sides, 256 threads.
 template <typename TE>
 __global__ __launch_bounds__(256) void gather_transpose_kernel(const TE* __restrict__ src, TE* __restrict__ out,
                                                                const int32_t* __restrict__ map, int n_rows, int C,
                                                                int D, long long src_batch, long long out_batch) {
-    __shared__ TE tile[kTrTile][kTrTile + 1];
+    constexpr int V = 16 / sizeof(TE);        // elements per 16-byte vector
+    constexpr int NV = kTrTile / V;           // vectors per tile row
+    __shared__ TE tile[kTrTile][kTrTile + 2];
     const int c0 = blockIdx.x * kTrTile, d0 = blockIdx.y * kTrTile;
     src += blockIdx.z * src_batch;
     out += blockIdx.z * out_batch;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    // read: rows c (one per iteration), columns d coalesced
-    for (int cc = ty; cc < kTrTile; cc += 4) {
-        const int c = c0 + cc;
+    for (int i = threadIdx.x; i < kTrTile * NV; i += 256) {
+        const int r = i / NV, cv = i % NV;
+        const int c = c0 + r, d = d0 + cv * V;
         int row = -1;
         if (c < C) row = map ? map[c] : (c < n_rows ? c : -1);
-        const int d = d0 + tx;
-        tile[cc][tx] = (row >= 0 && d < D) ? src[(size_t)row * D + d] : (TE)0;
+        uint4 q = make_uint4(0u, 0u, 0u, 0u);
+        if (row >= 0 && d < D) q = *reinterpret_cast<const uint4*>(src + (size_t)row * D + d);
+        const TE* e = reinterpret_cast<const TE*>(&q);
+#pragma unroll
+        for (int j = 0; j < V; ++j) tile[r][cv * V + j] = e[j];
     }
     __syncthreads();
-    // write: rows d, columns c coalesced
-    for (int dd = ty; dd < kTrTile; dd += 4) {
-        const int d = d0 + dd, c = c0 + tx;
-        if (d < D && c < C) out[(size_t)d * C + c] = tile[tx][dd];
+    for (int i = threadIdx.x; i < kTrTile * NV; i += 256) {
+        const int dd = i / NV, cg = i % NV;
+        const int d = d0 + dd, c = c0 + cg * V;
+        if (d >= D || c >= C) continue;
+        uint4 q;
+        TE* e = reinterpret_cast<TE*>(&q);
+#pragma unroll
+        for (int j = 0; j < V; ++j) e[j] = tile[cg * V + j][dd];
+        *reinterpret_cast<uint4*>(out + (size_t)d * C + c) = q;
     }
 }
 
@@ -211,39 +221,65 @@ __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 
 constexpr int kBankRows = 16;   // bank rows per workgroup
 constexpr int kBankT = 64;      // tokens staged per step
+constexpr int kBankCols = 4;    // hidden columns per thread
+constexpr int kBankSplit = 8;   // token ranges summed separately, then in order
 
-// dbank[j][h] = sum over t (ascending) of dz[t][j] * x[t][h], fp32.
-// grid (ceil(H/256), ceil(NE/16)); thread h = 256*bx + tid.
+// part[ts][j][h] = sum over t in token range ts (ascending) of dz[t][j] * x[t][h];
+// grid (ceil(H/256), ceil(NE/16), kBankSplit), 64 threads x 4 columns.
 template <typename TX>
-__global__ __launch_bounds__(256) void dbank_kernel(const float* __restrict__ dz, const TX* __restrict__ x, int T,
-                                                    int H, int NE, float* __restrict__ dbank) {
+__global__ __launch_bounds__(64) void dbank_partial_kernel(const float* __restrict__ dz, const TX* __restrict__ x,
+                                                           int T, int H, int NE, float* __restrict__ part) {
     __shared__ float zs[kBankT][kBankRows];
-    const int h = blockIdx.x * 256 + threadIdx.x;
+    const int h0 = blockIdx.x * 64 * kBankCols + threadIdx.x * kBankCols;
     const int j0 = blockIdx.y * kBankRows;
-    float acc[kBankRows];
+    const int tlen = (T + kBankSplit - 1) / kBankSplit;
+    const int tb = blockIdx.z * tlen, te = min(T, tb + tlen);
+    float acc[kBankRows][kBankCols];
 #pragma unroll
-    for (int j = 0; j < kBankRows; ++j) acc[j] = 0.f;
-    for (int t0 = 0; t0 < T; t0 += kBankT) {
+    for (int j = 0; j < kBankRows; ++j)
+#pragma unroll
+        for (int c = 0; c < kBankCols; ++c) acc[j][c] = 0.f;
+    for (int t0 = tb; t0 < te; t0 += kBankT) {
         __syncthreads();
-        for (int i = threadIdx.x; i < kBankT * kBankRows; i += 256) {
+        for (int i = threadIdx.x; i < kBankT * kBankRows; i += 64) {
             const int tt = t0 + i / kBankRows, j = j0 + i % kBankRows;
-            zs[i / kBankRows][i % kBankRows] = (tt < T && j < NE) ? dz[(size_t)tt * NE + j] : 0.f;
+            zs[i / kBankRows][i % kBankRows] = (tt < te && j < NE) ? dz[(size_t)tt * NE + j] : 0.f;
         }
         __syncthreads();
-        if (h < H) {
-            const int tn = min(kBankT, T - t0);
+        if (h0 < H) {
+            const int tn = min(kBankT, te - t0);
             for (int tt = 0; tt < tn; ++tt) {
-                const float xv = to_f32<TX>(x[(size_t)(t0 + tt) * H + h]);
+                const TX* xr = x + (size_t)(t0 + tt) * H + h0;
+                float xv[kBankCols];
 #pragma unroll
-                for (int j = 0; j < kBankRows; ++j) acc[j] += zs[tt][j] * xv;
+                for (int c = 0; c < kBankCols; ++c) xv[c] = to_f32<TX>(xr[c]);
+#pragma unroll
+                for (int j = 0; j < kBankRows; ++j) {
+                    const float z = zs[tt][j];
+#pragma unroll
+                    for (int c = 0; c < kBankCols; ++c) acc[j][c] += z * xv[c];
+                }
             }
         }
     }
-    if (h < H) {
+    if (h0 < H) {
 #pragma unroll
         for (int j = 0; j < kBankRows; ++j)
-            if (j0 + j < NE) dbank[(size_t)(j0 + j) * H + h] = acc[j];
+            if (j0 + j < NE) {
+                float* o = part + ((size_t)blockIdx.z * NE + j0 + j) * H + h0;
+#pragma unroll
+                for (int c = 0; c < kBankCols; ++c) o[c] = acc[j][c];
+            }
     }
+}
+
+__global__ __launch_bounds__(256) void dbank_reduce_kernel(const float* __restrict__ part, int n, float* __restrict__ out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.f;
+#pragma unroll
+    for (int ts = 0; ts < kBankSplit; ++ts) s += part[(size_t)ts * n + i];
+    out[i] = s;
 }
 
 }  // namespace
@@ -294,14 +330,19 @@ hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, 
     return hipGetLastError();
 }
 
-hipError_t launch_dbank(int dtype, const float* dz, const void* x, int T, int H, int NE, float* dbank,
+hipError_t launch_dbank(int dtype, const float* dz, const void* x, int T, int H, int NE, float* part, float* dbank,
                         hipStream_t stream) {
-    dim3 grid((H + 255) / 256, (NE + kBankRows - 1) / kBankRows);
+    dim3 grid((H + 64 * kBankCols - 1) / (64 * kBankCols), (NE + kBankRows - 1) / kBankRows, kBankSplit);
     if (dtype == 1)
-        hipLaunchKernelGGL(dbank_kernel<bf16_t>, grid, dim3(256), 0, stream, dz, (const bf16_t*)x, T, H, NE, dbank);
+        hipLaunchKernelGGL(dbank_partial_kernel<bf16_t>, grid, dim3(64), 0, stream, dz, (const bf16_t*)x, T, H, NE,
+                           part);
     else
-        hipLaunchKernelGGL(dbank_kernel<float>, grid, dim3(256), 0, stream, dz, (const float*)x, T, H, NE, dbank);
+        hipLaunchKernelGGL(dbank_partial_kernel<float>, grid, dim3(64), 0, stream, dz, (const float*)x, T, H, NE, part);
+    const int n = NE * H;
+    hipLaunchKernelGGL(dbank_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, part, n, dbank);
     return hipGetLastError();
 }
+
+int dbank_partial_floats(int H, int NE) { return kBankSplit * NE * H; }
 
 }  // namespace inkling

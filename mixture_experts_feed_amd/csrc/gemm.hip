@@ -39,7 +39,8 @@ namespace {
 //            partial sums of dact . silu(g) * u (the routing-weight gradient)
 // kModeWgrad: weight gradients, one problem per expert, K = that expert's rows
 enum { kModeGateUp = 0, kModeDown = 1, kModeGateUpRaw = 2, kModeDAct = 3, kModeWgrad = 4 };
-constexpr int kSpinLimit = 400;   // polls of a tile-round wait (about 100-400 us at most)
+constexpr int kSpinLimit = 400;
+constexpr int kWgradEpi = 256;    // K-equivalent cost of a weight-gradient tile's fp32 epilogue   // polls of a tile-round wait (about 100-400 us at most)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
@@ -374,7 +375,28 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     const long long cost_all = cost_s + (long long)nb_routed * a.K_r;
     auto range_start = [&](int x) -> int {
         if (x >= 8) return nb_real;
-        if constexpr (MODE == kModeWgrad) return (int)((long long)nb_real * x / 8);
+        if constexpr (MODE == kModeWgrad) {
+            // a tile of problem p costs its K plus kWgradEpi (the fp32 tile
+            // write); routed costs accumulate in poff
+            const int per_p = a.wg_mtiles * a.wg_ntiles, E = a.wg_E;
+            const long long routed = (long long)per_p * (a.poff[E] + (long long)E * kWgradEpi);
+            const long long total = routed + (long long)per_p * a.S * (a.K_s + kWgradEpi);
+            const long long c = total * x / 8;
+            if (c <= 0) return 0;
+            if (c >= routed) {
+                const long long per_tile = a.K_s + kWgradEpi;
+                return min(nb_real, E * per_p + (int)((c - routed + per_tile - 1) / per_tile));
+            }
+            int lo = 0, hi = E - 1;   // last problem p with cost(problems < p) <= c
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((long long)per_p * (a.poff[mid] + (long long)mid * kWgradEpi) <= c) lo = mid;
+                else hi = mid - 1;
+            }
+            const long long before = (long long)per_p * (a.poff[lo] + (long long)lo * kWgradEpi);
+            const long long per_tile = (long long)(a.poff[lo + 1] - a.poff[lo]) + kWgradEpi;
+            return min(nb_real, lo * per_p + (int)min<long long>(per_p, (c - before + per_tile - 1) / per_tile));
+        }
         const long long c = cost_all * x / 8;
         if (c <= 0) return 0;                                   // also K_s == 0 (no shared blocks)
         if (c <= cost_s) return (int)((c + a.K_s - 1) / a.K_s);
@@ -827,9 +849,8 @@ int num_cus() {
 template <typename TE, int MODE>
 hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t stream) {
     if (max_tiles <= 0) return hipSuccess;
-    // persistent: at most one workgroup per CU (LDS), a multiple of the 8 XCDs;
-    // weight gradients (tiles of very different K) take one tile per workgroup
-    int grid = MODE == kModeWgrad ? max_tiles : std::min(max_tiles, num_cus() * (cfg == 0 ? 1 : kDecodeGridPerCU));
+    // persistent: at most one workgroup per CU (LDS), a multiple of the 8 XCDs
+    int grid = std::min(max_tiles, num_cus() * (cfg == 0 ? 1 : kDecodeGridPerCU));
     grid = (grid + 7) / 8 * 8;
     constexpr int kSync = MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kPrefillSyncGateUp
                           : MODE == kModeDown ? kPrefillSyncDown : 0;

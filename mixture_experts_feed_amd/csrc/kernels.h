@@ -114,8 +114,10 @@ hipError_t launch_router_backward(const double* zpart, int ksplit, const int32_t
 hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, const int32_t* pos,
                              const int32_t* topk_idx, const float* dzc, const float* bank, void* dx, int T, int H,
                              int E, int S, int k, hipStream_t stream);
-hipError_t launch_dbank(int dtype, const float* dz, const void* x, int T, int H, int NE, float* dbank,
+// d bank = dz^T x (fp32), as kBankSplit token-range partials summed in order
+hipError_t launch_dbank(int dtype, const float* dz, const void* x, int T, int H, int NE, float* part, float* dbank,
                         hipStream_t stream);
+int dbank_partial_floats(int H, int NE);
 
 // gamma[t] = value for t < T; the GEMM round counters zeroed (the dense MLP's
 // stand-in for the router and the permutation)
