@@ -531,6 +531,24 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     constexpr int A_STEP = 16 * ROWB;               // bytes between a wave's weight-row blocks
     constexpr int B_STEP = 16 * WM * ROWB;          // bytes between a wave's token blocks
 
+    // Tile-round rendezvous of an XCD (SYNC): every workgroup counts each tile
+    // it finishes on its XCD's counter and waits, for at most kSpinLimit polls,
+    // until every workgroup of its round has finished, so that the workgroups
+    // that share tiles through L2 start the next round together.  (Meeting
+    // also every 4-32 K stages inside a tile was measured slower.)
+    int sync_round = 0;
+    auto rendezvous = [&](long long target, bool wait) __attribute__((always_inline)) {
+        if (tid == 0) {
+            int32_t* ctr = a.round_counter + xcd;
+            __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wait)
+                for (int it = 0; it < kSpinLimit; ++it) {
+                    if (__hip_atomic_fetch_add(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+        }
+    };
+
     // NJ: 16-row token blocks computed (blocks past the last valid row skipped).
     //
     // Work of a stage = KS k-steps x 2 halves of the token blocks (half-steps).
@@ -630,6 +648,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 
     while (true) {
         const int nk = cur.K / BK;
+        if constexpr (SYNC) sync_round = (L - L_beg) / nloc;
         // token blocks / weight-row blocks of this wave that hold valid rows
         const int nvb_all = (cur.rows_valid + 15) >> 4;
         const int nvb = min(FM, max(0, (nvb_all - wm + WM - 1) / WM));
@@ -651,23 +670,9 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         L += nloc;
         const bool has_next = L < L_end;
         if constexpr (SYNC) {
-            // Tile rounds of an XCD: the workgroups that share operands through
-            // its L2 start round r + 1 together, once round r is finished by all
-            // (bounded wait: after kSpinLimit polls the workgroup goes on).
-            if (tid == 0) {
-                int32_t* ctr = a.round_counter + xcd;
-                __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (has_next) {
-                    // tiles in rounds 0..r of this XCD (round r just finished; with a
-                    // next tile, rounds 0..r are all full)
-                    const int done = L - nloc - L_beg;
-                    const int target = done - done % nloc + nloc;
-                    for (int it = 0; it < kSpinLimit; ++it) {
-                        if (__hip_atomic_fetch_add(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                }
-            }
+            // end of the tile: round r + 1 starts once round r is done by all
+            // (with a next tile, rounds 0..r are full)
+            rendezvous((long long)nloc * (sync_round + 1), has_next);
         }
         wait_lgkmcnt0();
         barrier_keep_loads();
