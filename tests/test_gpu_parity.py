@@ -89,6 +89,7 @@ EDGE = {
     "inkling_defaults_E256_k6": wl.custom(T=512, hidden=256, n_routed=256, top_k=6, n_shared=2, intermediate=128,
                                           route_scale=8.0),
     "single_token": wl.custom(T=1, hidden=128, n_routed=8, top_k=2, n_shared=1, intermediate=64),
+    "minimal_width_h64_i64": wl.custom(T=90, hidden=64, n_routed=6, top_k=3, n_shared=3, intermediate=64),
 }
 
 
@@ -174,6 +175,26 @@ def _sampled_parity(name, experts, n_sample=24):
     counts = routing["expert_counts"].cpu().numpy()
     _say(f"[parity] {name} ok: band={band} rows={len(rows)} max_err/rms={rel:.2e} "
          f"empty={int((counts == 0).sum())} max_count={int(counts.max())}")
+
+
+def test_large_token_count_T65536():
+    """T = 65536 tokens x top-8 (524288 routed rows) at hidden 1024: routing of
+    every token bit-exact, outputs of sampled tokens against the oracle."""
+    w = wl.custom("large_T", T=65536, hidden=1024, n_routed=64, top_k=8, n_shared=1, intermediate=512,
+                  route_scale=2.5, gate_dist=("uniform", 0.05), bias_dist=("uniform", 0.05))
+    _say(f"[parity] {w}")
+    inp = _inputs(w)
+    out, routing = _run_both(w, inp)
+    ref = P.oracle_route(inp, w.top_k)
+    band = P.check_routing(routing, ref, w.top_k)
+    rng = np.random.default_rng(2)
+    rows = sorted(set([0, 1, w.T - 2, w.T - 1] + rng.choice(w.T, size=28, replace=False).tolist()))
+    o_ref, _ = oracle.moe_forward(P.host(inp["x"]), P.host(inp["gate_bank"]), P.host(inp["bias"]),
+                                  P.HostExperts(inp["w_gu"]), P.HostExperts(inp["w_d"]),
+                                  P.HostExperts(inp["wsh_gu"]), P.HostExperts(inp["wsh_d"]),
+                                  w.top_k, w.route_scale, w.global_scale, tokens=rows, routing=ref)
+    rel = P.check_output(out, o_ref, w.dtype, rows=rows)
+    _say(f"[parity] large_T ok: band={band} rows={len(rows)} max_err/rms={rel:.2e}")
 
 
 def test_decode_h6144(h6144_experts):
