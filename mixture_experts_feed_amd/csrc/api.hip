@@ -51,7 +51,7 @@ Layout make_layout(const inkling_moe_dims_t* d) {
     const int NE = E + S;
     L.ksplit = router_ksplit((int)T, H, NE);
     L.W = (int)((T + 63) / 64);
-    L.cfg = gemm_cfg_for(d->dtype, (int)T, H, E, k, I);
+    L.cfg = gemm_cfg_for((int)T, E, k);
     L.bm = gemm_cfg_bm(L.cfg);
     L.max_tiles = (int)((T * k + L.bm - 1) / L.bm) + E;
     size_t o = 0;
@@ -358,7 +358,7 @@ int inkling_dense_mlp_forward(const inkling_dense_dims_t* dims, const void* x, c
     MoeGemmParams p = {};
     p.dtype = dims->dtype == INKLING_BF16 ? 1 : 0;
     p.out_dtype = dims->out_dtype == INKLING_BF16 ? 1 : 0;
-    p.cfg = gemm_cfg_for(p.dtype, T, H, 1, 1, I);
+    p.cfg = gemm_cfg_for(T, 1, 1);
     p.T = T;
     p.H = H;
     p.E = 0;

@@ -11,16 +11,18 @@
 // 1::2 up), so SwiGLU and the routing-weight scale are applied in registers.
 //
 // Launches per forward:
-//   gate_up       routed tiles (rows gathered through the expert-sorted token
-//                 list, scaled by that slot's gamma) and shared tiles (all
-//                 tokens against the S shared experts concatenated along N,
-//                 scaled by the token's shared gamma) -> act_r, act_sh;
-//   down routed   act_r rows of each expert -> y, one fp32 row per routed slot
-//                 t*k + i (rows of a token are adjacent);
-//   down shared   act_sh [T][S*I] against the shared down weights concatenated
-//                 along K, so the sum over shared experts happens inside the
-//                 reduction -> ysh [T][H] fp32;
-//   combine       out[t] = ysh[t] + sum_i y[t*k + i], rounded once.
+//   gate_up  routed tiles (rows gathered through the expert-sorted token list,
+//            scaled by that slot's gamma) and shared tiles (all tokens against
+//            the S shared experts concatenated along N, scaled by the token's
+//            shared gamma) -> act_r, act_sh;
+//   down     routed: act_r rows of each expert -> y, one fp32 row per routed
+//            slot t*k + i (rows of a token are adjacent); shared: act_sh
+//            [T][S*I] against the shared down weights concatenated along K, so
+//            the sum over shared experts happens inside the reduction -> ysh
+//            [T][H] fp32; one launch, shared tiles first;
+//   combine  out[t] = ysh[t] + sum_i y[t*k + i], rounded once.
+// The backward reuses the same kernel with other epilogues and operands (see
+// the modes below and backward.hip).
 #include <algorithm>
 #include <type_traits>
 
@@ -284,11 +286,12 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
 // tiles on its XCD (blocks are dealt to the 8 XCDs round-robin, so workgroups
 // that run side by side on one XCD share that range's operands through its L2)
 // and walks the range with stride = workgroups per XCD.  BN weight rows x BM
-// token rows per tile; WN x WM waves (8, two per SIMD); STAGES LDS pipeline
-// stages of ROWB bytes of K per row, filled by direct global->LDS loads.  TE:
-// operand and intermediate type.
+// token rows per tile; WN x WM waves (8, two per SIMD); SA weight and SB token
+// LDS pipeline stages of ROWB bytes of K per row, filled by direct global->LDS
+// loads.  TE: operand and intermediate type.
 //
-// Each stage is its own __shared__ array and the K loop is unrolled by STAGES,
+// Each stage is its own __shared__ array and the K loop is unrolled by
+// lcm(SA, SB),
 // so every LDS read and every LDS-DMA target is a distinct, statically known
 // object: the compiler then needs no wait on in-flight DMA before reading a
 // stage that is already complete.  The first stages of the next tile are
@@ -829,7 +832,7 @@ __global__ __launch_bounds__(256) void dense_prep_kernel(float* __restrict__ gam
 // cfg 0 (many rows per expert): 256 weight rows x 256 tokens, 8 waves (two per
 //       SIMD) as 4 along the weight rows x 2 along the tokens, each 64 rows x
 //       128 tokens (token blocks interleaved), 2 stages of 128-byte rows.
-// cfg 1 (few rows per expert, decode): 256 weight rows x 16 tokens, 8 waves
+// cfg 1 (few rows per expert, decode): 128 weight rows x 16 tokens, 8 waves
 //       along the weight rows, 4 stages.
 constexpr int kPrefillStagesA = 2, kPrefillStagesB = 2, kPrefillRowB = 128;
 // tile-round rendezvous per XCD: pays off for the long-K gate_up tiles only
@@ -894,8 +897,7 @@ GemmKArgs base_args(const MoeGemmParams& p) {
 
 }  // namespace
 
-int gemm_cfg_for(int dtype, int T, int H, int E, int k, int I) {
-    (void)dtype; (void)H; (void)I;
+int gemm_cfg_for(int T, int E, int k) {
     const double rows_per_expert = (double)T * k / E;
     return rows_per_expert <= 48.0 ? 1 : 0;
 }

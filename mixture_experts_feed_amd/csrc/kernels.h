@@ -59,7 +59,9 @@ struct MoeGemmParams {
     int has_routed;            // 0: shared tiles only (dense MLP); tiles / num_tiles unused
     int max_routed_tiles;
 };
-int gemm_cfg_for(int dtype, int T, int H, int E, int k, int I);
+// tile configuration: 0 (256 x 256 tiles) unless experts receive <= 48 rows on
+// average, then 1 (128 weight rows x 16 tokens)
+int gemm_cfg_for(int T, int E, int k);
 int gemm_cfg_bm(int cfg);
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
 // routed (act_r -> y) and shared (act_sh -> ysh) down projections, one launch
