@@ -189,6 +189,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the InklingDenseMLP line")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward line")
+    ap.add_argument("--no-others", action="store_true", help="skip the small and skewed workload lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -300,6 +301,31 @@ def main():
                             "bytes_alg": bytes_alg, "n_touched_experts": n_touched,
                             "stage_ms": {n: round(dstage[i], 4) for i, n in enumerate(B.STAGES)}}
         log(f"[bench] decode {dms:.3f} ms, {result['decode']['hbm_GBps']} GB/s")
+
+    if not args.no_others and w.name == "prefill_h6144":
+        # the other two TFLOP/s workloads: skewed routing (same weights) and the small bf16 shape
+        result["other_workloads"] = {}
+        for oname in ("skewed_h6144", "small_bf16"):
+            ow = wl.WORKLOADS[oname]
+            oinp = wl.make_inputs(ow, device=dev, with_experts=ow.hidden != w.hidden)
+            if ow.hidden == w.hidden:
+                for k in ("w_gu", "w_d", "wsh_gu", "wsh_d"):
+                    oinp[k] = inp[k]
+            odims = B.make_dims(ow.T, ow.hidden, ow.n_routed, ow.top_k, ow.n_shared, ow.intermediate, ow.torch_dtype)
+            ows = B.alloc_workspace(odims, dev)
+            oout = torch.empty_like(oinp["x"])
+
+            def ocall():
+                B.forward(oinp["x"], oinp["gate_bank"], oinp["bias"], oinp["w_gu"], oinp["w_d"], oinp["wsh_gu"],
+                          oinp["wsh_d"], ow.top_k, ow.route_scale, ow.global_scale, out=oout, workspace=ows)
+
+            oms, _ = run_timed(torch, B, ocall, args.steps, args.warmup, events)
+            otf = ow.flops_alg() / (oms * 1e-3) / 1e12
+            result["other_workloads"][oname] = {"T": ow.T, "hidden": ow.hidden, "ms_per_step": round(oms, 4),
+                                                "TFLOP_s": round(otf, 2), "tokens_per_s": round(ow.T / (oms * 1e-3), 1),
+                                                "frac_of_peak": round(otf / PEAK_BF16_TFLOPS, 4)}
+            log(f"[bench] {oname} {oms:.3f} ms, {otf:.1f} TFLOP/s")
+            del oinp, ows, oout
 
     if not args.no_dense:
         # InklingDenseMLP of the first layer (intermediate 24576) on the same token count
