@@ -146,9 +146,8 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
 // ---- backward -----------------------------------------------------------------
 struct BwdLayout {
     Layout F;   // the forward's routing and row buffers (y / ysh hold the dx rows)
-    int Cmax, Tpad;
-    size_t h_r, h_sh, dh_r, dh_sh, wdT, wshdT, wguT, wshguT, dgp_r, dgp_sh, dz, dzc, poff, col_row, col_tok;
-    size_t GsT, xsT, aT, dhT, GT, xT, a_shT, dh_shT, dbank_part, total;
+    int Tpad;
+    size_t h_r, h_sh, dh_r, dh_sh, dgp_r, dgp_sh, dz, dzc, poff, x_sorted, dout_sorted, zero, dbank_part, total;
 };
 
 BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
@@ -162,9 +161,7 @@ BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
     B.F.max_tiles = (int)((d->T * d->top_k + B.F.bm - 1) / B.F.bm) + d->n_routed;
     const size_t T = (size_t)d->T, E = d->n_routed, S = d->n_shared, k = d->top_k, H = d->hidden, I = d->intermediate;
     const size_t es = d->dtype == INKLING_BF16 ? 2 : 4;
-    B.Cmax = (int)((T * k + 64 * E + 63) / 64 * 64);
     B.Tpad = (int)((T + 63) / 64 * 64);
-    const size_t C = (size_t)B.Cmax, Tp = (size_t)B.Tpad;
     size_t o = B.F.total;
     auto take = [&](size_t bytes) {
         size_t at = o;
@@ -175,25 +172,14 @@ BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
     B.h_sh = take(T * S * 2 * I * 4);
     B.dh_r = take(T * k * 2 * I * es);
     B.dh_sh = take(T * S * 2 * I * es);
-    B.wdT = take(E * I * H * es);
-    B.wshdT = take(S * I * H * es);
-    B.wguT = take(E * 2 * I * H * es);
-    B.wshguT = take(S * 2 * I * H * es);
     B.dgp_r = take(T * k * (I / 64) * 4);
     B.dgp_sh = take(T * S * (I / 64) * 4);
     B.dz = take(T * (E + S) * 4);
     B.dzc = take(T * (k + S) * 4);
     B.poff = take((E + 1) * 4);
-    B.col_row = take(C * 4);
-    B.col_tok = take(C * 4);
-    B.GsT = take(H * C * es);
-    B.xsT = take(H * C * es);
-    B.aT = take(I * C * es);
-    B.dhT = take(2 * I * C * es);
-    B.GT = take(H * Tp * es);
-    B.xT = take(H * Tp * es);
-    B.a_shT = take(S * I * Tp * es);
-    B.dh_shT = take(S * 2 * I * Tp * es);
+    B.x_sorted = take(T * k * H * es);
+    B.dout_sorted = take(T * k * H * es);
+    B.zero = take(std::max(H, 2 * I) * 4);
     B.dbank_part = take((size_t)dbank_partial_floats((int)H, (int)(E + S)) * 4);
     B.total = o;
     return B;
@@ -429,9 +415,7 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     rc = run_route(dims, L, x, gate, padding_mask, rb, true, workspace, s);
     if (rc != INKLING_OK) return rc;
     int32_t* poff = at<int32_t>(workspace, B.poff);
-    int32_t* col_row = at<int32_t>(workspace, B.col_row);
-    int32_t* col_tok = at<int32_t>(workspace, B.col_tok);
-    HIP_TRY(launch_column_map(rb.counts, rb.offsets, rb.row_token, E, B.Cmax, poff, col_row, col_tok, s));
+    HIP_TRY(launch_padded_offsets(rb.counts, E, poff, s));
 
     MoeGemmParams p = {};
     p.dtype = dt;
@@ -465,17 +449,8 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     void* h_sh = at<void>(workspace, B.h_sh);
     HIP_TRY(launch_gate_up_raw(p, h_r, h_sh, s));
 
-    // 3. transposed down projections; dact and the SwiGLU backward
-    void* wdT = at<void>(workspace, B.wdT);
-    void* wshdT = at<void>(workspace, B.wshdT);
-    HIP_TRY(launch_gather_transpose(dt, w->routed_down, wdT, nullptr, H, H, I, E, (long long)H * I, (long long)I * H,
-                                    s));
-    if (S > 0)
-        HIP_TRY(launch_gather_transpose(dt, w->shared_down, wshdT, nullptr, H, H, I, S, (long long)H * I,
-                                        (long long)I * H, s));
+    // 3. dact and the SwiGLU backward
     BwdActBufs ab = {};
-    ab.wdT = wdT;
-    ab.wshdT = wshdT;
     ab.dout = dout;
     ab.h_r = h_r;
     ab.h_sh = h_sh;
@@ -493,79 +468,61 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     HIP_TRY(launch_router_backward(at<double>(workspace, L.zpart), L.ksplit, rb.topk_idx, rb.pos, ab.dgp_r, ab.dgp_sh,
                                    T, E, S, k, I, gate->route_scale, gate->global_scale, dz, dzc, s));
 
-    // 5. dx rows: transposed gate_up projections against dh (the down-GEMM shape,
+    // 5. dx rows: the gate_up projections against dh (the down-GEMM shape,
     //    K = 2I); then dx = shared + routed rows + gate term, rounded once
-    void* wguT = at<void>(workspace, B.wguT);
-    void* wshguT = at<void>(workspace, B.wshguT);
-    HIP_TRY(launch_gather_transpose(dt, w->routed_gate_up, wguT, nullptr, 2 * I, 2 * I, H, E, (long long)2 * I * H,
-                                    (long long)H * 2 * I, s));
-    if (S > 0)
-        HIP_TRY(launch_gather_transpose(dt, w->shared_gate_up, wshguT, nullptr, 2 * I, 2 * I, H, S,
-                                        (long long)2 * I * H, (long long)H * 2 * I, s));
-    MoeGemmParams q = p;
-    q.I = 2 * I;
-    q.w_d = wguT;
-    q.wsh_d = wshguT;
-    q.act_r = ab.dh_r;
-    q.act_sh = ab.dh_sh;
-    q.y = at<void>(workspace, L.y);
-    q.ysh = at<void>(workspace, L.ysh);
-    HIP_TRY(launch_down(q, s));
+    HIP_TRY(launch_dx(p, ab.dh_r, ab.dh_sh, at<void>(workspace, L.y), at<void>(workspace, L.ysh), s));
     HIP_TRY(launch_dx_combine(p.out_dtype, at<float>(workspace, L.y), S > 0 ? at<float>(workspace, L.ysh) : nullptr,
                               rb.pos, rb.topk_idx, dzc, gate->gate_bank, dx, T, H, E, S, k, s));
 
     // 6. gate bank gradient
     HIP_TRY(launch_dbank(dt, dz, x, T, H, E + S, at<float>(workspace, B.dbank_part), g->d_gate_bank, s));
 
-    // 7. weight gradients: operands transposed so that K (rows of an expert,
-    //    each expert's columns padded to 64 with zeros; or tokens) is contiguous
-    const int C = B.Cmax, Tp = B.Tpad;
-    void* GsT = at<void>(workspace, B.GsT);
-    void* xsT = at<void>(workspace, B.xsT);
-    void* aT = at<void>(workspace, B.aT);
-    void* dhT = at<void>(workspace, B.dhT);
-    void* GT = at<void>(workspace, B.GT);
-    void* xT = at<void>(workspace, B.xT);
-    void* a_shT = at<void>(workspace, B.a_shT);
-    void* dh_shT = at<void>(workspace, B.dh_shT);
-    HIP_TRY(launch_gather_transpose(dt, dout, GsT, col_tok, 0, C, H, 1, 0, 0, s));
-    HIP_TRY(launch_gather_transpose(dt, x, xsT, col_tok, 0, C, H, 1, 0, 0, s));
-    HIP_TRY(launch_gather_transpose(dt, ab.a_r, aT, col_row, 0, C, I, 1, 0, 0, s));
-    HIP_TRY(launch_gather_transpose(dt, ab.dh_r, dhT, col_row, 0, C, 2 * I, 1, 0, 0, s));
-    if (S > 0) {
-        HIP_TRY(launch_gather_transpose(dt, dout, GT, nullptr, T, Tp, H, 1, 0, 0, s));
-        HIP_TRY(launch_gather_transpose(dt, x, xT, nullptr, T, Tp, H, 1, 0, 0, s));
-        HIP_TRY(launch_gather_transpose(dt, ab.a_sh, a_shT, nullptr, T, Tp, S * I, 1, 0, 0, s));
-        HIP_TRY(launch_gather_transpose(dt, ab.dh_sh, dh_shT, nullptr, T, Tp, S * 2 * I, 1, 0, 0, s));
-    }
+    // 7. weight gradients, contracting over the rows of an expert (or the
+    //    tokens): the expert-sorted rows of a and dh as they are, x and dout
+    //    gathered into expert order
+    void* x_sorted = at<void>(workspace, B.x_sorted);
+    void* dout_sorted = at<void>(workspace, B.dout_sorted);
+    void* zero = at<void>(workspace, B.zero);
+    HIP_TRY(launch_zero_words(static_cast<uint32_t*>(zero), (size_t)std::max(H, 2 * I), s));
+    HIP_TRY(launch_gather_rows(dt, x, rb.row_token, rb.offsets, E, T * k, H, x_sorted, s));
+    HIP_TRY(launch_gather_rows(dt, dout, rb.row_token, rb.offsets, E, T * k, H, dout_sorted, s));
     WgradParams wd = {};   // d down[e][h][i] = sum_r dout[t(r)][h] a[r][i]
     wd.dtype = dt;
     wd.E = E;
     wd.S = S;
     wd.M = H;
     wd.N = I;
-    wd.B_r = GsT;
-    wd.A_r = aT;
+    wd.T = T;
     wd.poff = poff;
-    wd.ld_r = C;
-    wd.B_s = GT;
-    wd.A_s = a_shT;
-    wd.ld_s = Tp;
-    wd.K_s = Tp;
-    wd.a_sh_stride = (long long)I * Tp;
+    wd.offsets = rb.offsets;
+    wd.zero = zero;
+    wd.A_r = ab.a_r;
+    wd.lda_r = I;
+    wd.B_r = dout_sorted;
+    wd.ldb_r = H;
+    wd.A_s = ab.a_sh;      // [T][S*I], expert s at column s*I
+    wd.lda_s = S * I;
+    wd.a_sh_stride = I;
+    wd.B_s = dout;
+    wd.ldb_s = H;
     wd.b_sh_stride = 0;
+    wd.K_s = B.Tpad;
     wd.out_r = g->d_routed_down;
     wd.out_s = g->d_shared_down;
     HIP_TRY(launch_wgrad(wd, s));
     WgradParams wg = wd;   // d gate_up[e][n][h] = sum_r dh[r][n] x[t(r)][h]
     wg.M = 2 * I;
     wg.N = H;
-    wg.B_r = dhT;
-    wg.A_r = xsT;
-    wg.B_s = dh_shT;
-    wg.A_s = xT;
+    wg.A_r = x_sorted;
+    wg.lda_r = H;
+    wg.B_r = ab.dh_r;
+    wg.ldb_r = 2 * I;
+    wg.A_s = x;
+    wg.lda_s = H;
     wg.a_sh_stride = 0;
-    wg.b_sh_stride = (long long)2 * I * Tp;
+    wg.B_s = ab.dh_sh;     // [T][S*2I], expert s at column s*2I
+    wg.ldb_s = S * 2 * I;
+    wg.b_sh_stride = (long long)2 * I;
     wg.out_r = g->d_routed_gate_up;
     wg.out_s = g->d_shared_gate_up;
     HIP_TRY(launch_wgrad(wg, s));

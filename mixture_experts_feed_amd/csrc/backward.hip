@@ -21,44 +21,25 @@ namespace inkling {
 
 namespace {
 
-constexpr int kTrTile = 64;
-
-// out_b[d][c] = src_b[row(c)][d] for d < D, c < C, with row(c) = map[c]
-// (map != NULL; -1 gives 0) or c (c < n_rows, else 0).  src rows have D
-// elements, out rows C; C and D are multiples of 64.  64x64 tiles through LDS,
-// 16-byte loads and stores on both sides, 256 threads.
+// out[r] = src[row_token[r]] for r < offsets[E]: rows of D elements (D a
+// multiple of 64), 16-byte vectors, one row per block iteration.
 template <typename TE>
-__global__ __launch_bounds__(256) void gather_transpose_kernel(const TE* __restrict__ src, TE* __restrict__ out,
-                                                               const int32_t* __restrict__ map, int n_rows, int C,
-                                                               int D, long long src_batch, long long out_batch) {
-    constexpr int V = 16 / sizeof(TE);        // elements per 16-byte vector
-    constexpr int NV = kTrTile / V;           // vectors per tile row
-    __shared__ TE tile[kTrTile][kTrTile + 2];
-    const int c0 = blockIdx.x * kTrTile, d0 = blockIdx.y * kTrTile;
-    src += blockIdx.z * src_batch;
-    out += blockIdx.z * out_batch;
-    for (int i = threadIdx.x; i < kTrTile * NV; i += 256) {
-        const int r = i / NV, cv = i % NV;
-        const int c = c0 + r, d = d0 + cv * V;
-        int row = -1;
-        if (c < C) row = map ? map[c] : (c < n_rows ? c : -1);
-        uint4 q = make_uint4(0u, 0u, 0u, 0u);
-        if (row >= 0 && d < D) q = *reinterpret_cast<const uint4*>(src + (size_t)row * D + d);
-        const TE* e = reinterpret_cast<const TE*>(&q);
-#pragma unroll
-        for (int j = 0; j < V; ++j) tile[r][cv * V + j] = e[j];
+__global__ __launch_bounds__(256) void gather_rows_kernel(const TE* __restrict__ src,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ offsets, int E, int D,
+                                                          TE* __restrict__ out) {
+    constexpr int V = 16 / sizeof(TE);
+    const int rows = offsets[E];
+    const int nv = D / V;
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+        const uint4* s = reinterpret_cast<const uint4*>(src + (size_t)row_token[r] * D);
+        uint4* o = reinterpret_cast<uint4*>(out + (size_t)r * D);
+        for (int v = threadIdx.x; v < nv; v += 256) o[v] = s[v];
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kTrTile * NV; i += 256) {
-        const int dd = i / NV, cg = i % NV;
-        const int d = d0 + dd, c = c0 + cg * V;
-        if (d >= D || c >= C) continue;
-        uint4 q;
-        TE* e = reinterpret_cast<TE*>(&q);
-#pragma unroll
-        for (int j = 0; j < V; ++j) e[j] = tile[cg * V + j][dd];
-        *reinterpret_cast<uint4*>(out + (size_t)d * C + c) = q;
-    }
+}
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }
 
 // poff[e] = sum over e' < e of counts rounded up to 64 (poff[E] the total);
@@ -84,31 +65,6 @@ __global__ __launch_bounds__(1024) void padded_offsets_kernel(const int32_t* __r
         __syncthreads();
     }
     if (tid == 0) poff[E] = carry;
-}
-
-// For padded column c of expert e (poff[e] <= c < poff[e+1]): the sorted row
-// offsets[e] + (c - poff[e]) while inside the expert's count, else -1; and its
-// token.  Columns past poff[E] get -1.
-__global__ __launch_bounds__(256) void column_map_kernel(const int32_t* __restrict__ poff,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ row_token, int E, int C,
-                                                         int32_t* __restrict__ col_row,
-                                                         int32_t* __restrict__ col_tok) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= C) return;
-    int row = -1;
-    if (c < poff[E]) {
-        int lo = 0, hi = E - 1;   // last e with poff[e] <= c
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (poff[mid] <= c) lo = mid;
-            else hi = mid - 1;
-        }
-        const int j = c - poff[lo];
-        if (j < offsets[lo + 1] - offsets[lo]) row = offsets[lo] + j;
-    }
-    col_row[c] = row;
-    col_tok[c] = row >= 0 ? row_token[row] : -1;
 }
 
 // One wave per token: routing-weight gradients (sums of the 64-column
@@ -284,24 +240,28 @@ __global__ __launch_bounds__(256) void dbank_reduce_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_gather_transpose(int dtype, const void* src, void* out, const int32_t* map, int n_rows, int C,
-                                   int D, int batch, long long src_batch, long long out_batch, hipStream_t stream) {
-    if (C <= 0 || D <= 0 || batch <= 0) return hipSuccess;
-    dim3 grid((C + kTrTile - 1) / kTrTile, (D + kTrTile - 1) / kTrTile, batch);
+hipError_t launch_gather_rows(int dtype, const void* src, const int32_t* row_token, const int32_t* offsets, int E,
+                              int max_rows, int D, void* out, hipStream_t stream) {
+    if (max_rows <= 0 || D <= 0) return hipSuccess;
+    const int blocks = std::min(max_rows, 4096);
     if (dtype == 1)
-        hipLaunchKernelGGL(gather_transpose_kernel<bf16_t>, grid, dim3(256), 0, stream, (const bf16_t*)src,
-                           (bf16_t*)out, map, n_rows, C, D, src_batch, out_batch);
+        hipLaunchKernelGGL(gather_rows_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, (const bf16_t*)src,
+                           row_token, offsets, E, D, (bf16_t*)out);
     else
-        hipLaunchKernelGGL(gather_transpose_kernel<float>, grid, dim3(256), 0, stream, (const float*)src,
-                           (float*)out, map, n_rows, C, D, src_batch, out_batch);
+        hipLaunchKernelGGL(gather_rows_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)src,
+                           row_token, offsets, E, D, (float*)out);
     return hipGetLastError();
 }
 
-hipError_t launch_column_map(const int32_t* counts, const int32_t* offsets, const int32_t* row_token, int E, int C,
-                             int32_t* poff, int32_t* col_row, int32_t* col_tok, hipStream_t stream) {
+hipError_t launch_padded_offsets(const int32_t* counts, int E, int32_t* poff, hipStream_t stream) {
     hipLaunchKernelGGL(padded_offsets_kernel, dim3(1), dim3(1024), 0, stream, counts, E, poff);
-    hipLaunchKernelGGL(column_map_kernel, dim3((C + 255) / 256), dim3(256), 0, stream, poff, offsets, row_token, E, C,
-                       col_row, col_tok);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
 

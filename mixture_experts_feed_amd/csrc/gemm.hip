@@ -22,7 +22,12 @@
 //            [T][H] fp32; one launch, shared tiles first;
 //   combine  out[t] = ysh[t] + sum_i y[t*k + i], rounded once.
 // The backward reuses the same kernel with other epilogues and operands (see
-// the modes below and backward.hip).
+// the modes below and backward.hip).  Its products contract over the other
+// index of a stored matrix (the down weights over H, the gate_up weights over
+// 2I, activations over their rows), so those operands are read in their
+// stored [K][N] layout: K rows of N contiguous elements are copied to LDS as
+// they are, and the CDNA4 transposing LDS read (ds_read_b64_tr_b16) turns four
+// K rows of a column block into the per-lane K runs the MFMA takes.
 #include <algorithm>
 #include <type_traits>
 
@@ -40,7 +45,13 @@ namespace {
 //            dh = d[gate, up] (TE), a = gamma * silu(g) * u (TE) and per-64-column
 //            partial sums of dact . silu(g) * u (the routing-weight gradient)
 // kModeWgrad: weight gradients, one problem per expert, K = that expert's rows
-enum { kModeGateUp = 0, kModeDown = 1, kModeGateUpRaw = 2, kModeDAct = 3, kModeWgrad = 4 };
+// kModeDx: backward through gate_up: the down epilogue (fp32 rows)
+// A is read as [K][N] in kModeDAct, kModeDx and kModeWgrad, B in kModeWgrad.
+enum { kModeGateUp = 0, kModeDown = 1, kModeGateUpRaw = 2, kModeDAct = 3, kModeWgrad = 4, kModeDx = 5 };
+template <int MODE>
+constexpr bool a_kn() { return MODE == kModeDAct || MODE == kModeDx || MODE == kModeWgrad; }
+template <int MODE>
+constexpr bool b_kn() { return MODE == kModeWgrad; }
 constexpr int kSpinLimit = 400;   // polls of a tile-round wait (about 100-400 us at most)
 constexpr int kWgradEpi = 256;    // K-equivalent cost of a weight-gradient tile's fp32 epilogue
 // Cache policy of the weight (A) loads.  Tiles of at most 16 token rows (the
@@ -81,10 +92,17 @@ struct GemmKArgs {
     void* a_shared;            // [T][S*I]
     float* dgp_routed;         // [T*k][I/64]
     float* dgp_shared;         // [T][S*I/64]
-    // kModeWgrad: problems e < E (routed, K = padded rows of e at column
-    // offset poff[e]) then s < S (shared, K = K_s); out[m][n] = sum_k B[m][k] A[n][k]
-    const int32_t* poff;       // [E+1] padded column offsets
-    int ld_r, ld_s;            // row strides of the routed / shared operands
+    // operands read as [K][N]: row strides; the shared A of kModeDAct holds the
+    // S experts side by side along N (column n at element (n / a_segn_s) *
+    // a_segstride_s + n % a_segn_s of a row)
+    int lda_r, lda_s, ldb_r, ldb_s;
+    int a_segn_s;
+    long long a_segstride_s;
+    // kModeWgrad: problems e < E (routed: K = rows offsets[e].. of e, padded to
+    // poff[e+1] - poff[e]) then s < S (shared: K = K_s rows of which T are
+    // tokens); out[m][n] = sum_k B[k][m] A[k][n]; padding rows of B read `zero`
+    const int32_t* poff;       // [E+1] prefix sums of the padded row counts
+    const void* zero;          // a zero row, at least wg_M elements
     long long a_sh_stride, b_sh_stride;   // element offset of shared problem s in A / B
     int wg_E, wg_M, wg_N, wg_mtiles, wg_ntiles;
     float* w_out_routed;       // [E][M][N]
@@ -109,6 +127,20 @@ __device__ __forceinline__ void mma16<float>(f32x4_t& acc, const uint4& a, const
 }
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// One bf16 MFMA fragment (8 consecutive K of one column per lane) from a
+// [K][N] LDS stage: lane l of each 16-lane group addresses 4 columns of K row
+// (l/4)%4 at p, and ds_read_b64_tr_b16 hands lane l the 4 rows of column l%16;
+// the second read takes the next 4 rows.
+__device__ __forceinline__ uint4 read_tr16_frag(const uint8_t* p, int row_bytes) {
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p + 4 * row_bytes));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
 
 template <typename TE>
 __device__ __forceinline__ void store2(TE* p, float a, float b);
@@ -207,6 +239,9 @@ struct Tile {
     bool is_shared;
     int K, N, seg, n0, rows_valid, grow0, t0;
     int lda, ldb;        // row strides of A and B (elements)
+    int cnt;             // operands read as [K][N]: K rows that exist (K unless padded)
+    int segn;            // ... A column segments (see GemmKArgs::a_segn_s)
+    long long segstride;
     const TE* A;
     const TE* B;
     float* out;          // kModeWgrad: this problem's gradient [M][N]
@@ -218,6 +253,8 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
     t.grow0 = 0;
     t.t0 = 0;
     t.out = nullptr;
+    t.segn = 1;
+    t.segstride = 0;
     if constexpr (MODE == kModeWgrad) {
         const int per_p = a.wg_mtiles * a.wg_ntiles;
         const int pr = L / per_p;
@@ -229,21 +266,26 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
         t.n0 = nt * BN;
         t.N = a.wg_N;
         if (!t.is_shared) {
-            const int k0 = a.poff[pr];
-            t.K = a.poff[pr + 1] - k0;
-            t.A = reinterpret_cast<const TE*>(a.A_routed) + k0;
-            t.B = reinterpret_cast<const TE*>(a.B_routed) + k0;
-            t.lda = t.ldb = a.ld_r;
+            const int r0 = a.offsets[pr];
+            t.K = a.poff[pr + 1] - a.poff[pr];
+            t.cnt = a.offsets[pr + 1] - r0;
+            t.A = reinterpret_cast<const TE*>(a.A_routed) + (size_t)r0 * a.lda_r;
+            t.B = reinterpret_cast<const TE*>(a.B_routed) + (size_t)r0 * a.ldb_r;
+            t.lda = a.lda_r;
+            t.ldb = a.ldb_r;
             t.out = a.w_out_routed + (size_t)pr * a.wg_M * a.wg_N;
         } else {
             const int sx = pr - a.wg_E;
             t.K = a.K_s;
+            t.cnt = a.T;
             t.A = reinterpret_cast<const TE*>(a.A_shared) + sx * a.a_sh_stride;
             t.B = reinterpret_cast<const TE*>(a.B_shared) + sx * a.b_sh_stride;
-            t.lda = t.ldb = a.ld_s;
+            t.lda = a.lda_s;
+            t.ldb = a.ldb_s;
             t.out = a.w_out_shared + (size_t)sx * a.wg_M * a.wg_N;
         }
         t.seg = max(t.K, 1);
+        t.segn = t.N;
         return t;
     }
     t.is_shared = L < a.shared_blocks;
@@ -260,6 +302,11 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
         t.ldb = a.K_s;
         t.A = reinterpret_cast<const TE*>(a.A_shared);
         t.B = reinterpret_cast<const TE*>(a.B_shared);
+        if constexpr (a_kn<MODE>()) {
+            t.lda = a.lda_s;
+            t.segn = a.a_segn_s;
+            t.segstride = a.a_segstride_s;
+        }
     } else {
         // The blocks of expert e are [first tile of e, last + 1) x ntn_r; they are
         // walked column-major (all row tiles of e for weight tile 0, then 1, ...)
@@ -284,7 +331,12 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
         t.ldb = a.K_r;
         t.A = reinterpret_cast<const TE*>(a.A_routed) + (size_t)tl.expert * a.N_r * a.K_r;
         t.B = reinterpret_cast<const TE*>(a.B_routed);
+        if constexpr (a_kn<MODE>()) {
+            t.lda = a.lda_r;
+            t.segn = a.N_r;
+        }
     }
+    t.cnt = t.K;
     return t;
 }
 
@@ -327,6 +379,14 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     constexpr int A_PW = A_INS / NW, B_PW = (B_INS + NW - 1) / NW;
     static_assert(A_INS % NW == 0, "A loads spread evenly over the waves");
     constexpr int SMALL = 16;
+    // operands read as [K][N]: a stage holds BK rows of K, each the tile's BN
+    // (A) or BM (B) columns, filled by the same number of 1 KB wave loads
+    constexpr bool AKN = a_kn<MODE>(), BKN = b_kn<MODE>();
+    constexpr int RBA = BN * (int)sizeof(TE), RBB = BM * (int)sizeof(TE);   // bytes per K row
+    constexpr int CHA = RBA / 16, CHB = RBB / 16;                           // 16-byte chunks per K row
+    constexpr int RPIA = 1024 / RBA, RPIB = 1024 / RBB;                     // K rows per wave load
+    static_assert(!AKN || (RBA >= 256 && RBA <= 1024 && BK / RPIA == A_INS), "[K][N] A stage shape");
+    static_assert(!BKN || (RBB >= 256 && RBB <= 1024 && BK / RPIB == B_INS), "[K][N] B stage shape");
     // distinct LDS objects per weight stage and per token stage (unused ones
     // shrink to SMALL bytes)
     __shared__ __attribute__((aligned(16))) uint8_t sa0[A_BYTES];
@@ -423,27 +483,45 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     // position c ^ sw(r), which makes the fragment reads below conflict-free.
     // A wave load fills RPL rows: lane -> row lane / CH, chunk position lane % CH.
     auto sw = [](int r) { return CH == 4 ? ((r >> 1) & 3) : CH == 8 ? (r & 7) : (r & 15); };
+    // [K][N] stages: the 16-byte chunk c of K row r sits at chunk position
+    // c ^ swk(r); the rows that one transposing read touches differ in bits 0,
+    // 1 and 3, so their column blocks land on different banks.  (fp32 stages
+    // are not swizzled.)
+    auto swk = [](int r) { return sizeof(TE) == 2 ? ((r & 3) | ((r >> 1) & 4)) << 1 : 0; };
     const int lr = lane / CH, lp = lane % CH;
     const TE* a_src[A_PW];
     const TE* b_src[B_PW];
-    int a_k = 0, b_k = 0, rows_valid_ld = 1, seg_ld = 1;
+    int a_k = 0, b_k = 0, rows_valid_ld = 1, seg_ld = 1, cnt_ld = 0, lda_ld = 0, ldb_ld = 0, m0_ld = 0;
     size_t a_seg = 0, a_seg_step = 0;
     auto setup = [&](const Tile<TE>& t) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < A_PW; ++q) {
-            const int r = RPL * (wv + NW * q) + lr;
-            a_src[q] = t.A + (size_t)min(t.n0 + r, t.N - 1) * t.lda + (lp ^ sw(r)) * EPC;   // rows past N re-read N-1
+            if constexpr (AKN) {
+                const int r = RPIA * (wv + NW * q) + lane / CHA;   // K row within a stage
+                const int c = (lane % CHA) ^ swk(r);                // chunk this lane's LDS position holds
+                const int n = min(t.n0 + c * EPC, t.N - EPC);      // columns past N re-read the last chunk
+                a_src[q] = t.A + (long long)(n / t.segn) * t.segstride + n % t.segn + (size_t)r * t.lda;
+            } else {
+                const int r = RPL * (wv + NW * q) + lr;
+                a_src[q] = t.A + (size_t)min(t.n0 + r, t.N - 1) * t.lda + (lp ^ sw(r)) * EPC;   // rows past N re-read N-1
+            }
         }
 #pragma unroll
         for (int q = 0; q < B_PW; ++q) {
-            const int r = RPL * (wv + NW * q) + lr;
-            const int rr = min(r, t.rows_valid - 1);   // rows past the end re-read the last valid row
-            size_t row;
-            if (t.is_shared || MODE == kModeWgrad) row = (size_t)(t.t0 + rr);
-            else if (MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct)
-                row = (size_t)a.row_token[t.grow0 + rr];   // routed token rows, gathered
-            else row = (size_t)(t.grow0 + rr);
-            b_src[q] = t.B + row * t.ldb + (lp ^ sw(r)) * EPC;
+            if constexpr (BKN) {
+                const int r = RPIB * (wv + NW * q) + lane / CHB;
+                const int c = (lane % CHB) ^ swk(r);
+                b_src[q] = t.B + min(t.t0 + c * EPC, a.wg_M - EPC) + (size_t)r * t.ldb;
+            } else {
+                const int r = RPL * (wv + NW * q) + lr;
+                const int rr = min(r, t.rows_valid - 1);   // rows past the end re-read the last valid row
+                size_t row;
+                if (t.is_shared || MODE == kModeWgrad) row = (size_t)(t.t0 + rr);
+                else if (MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct)
+                    row = (size_t)a.row_token[t.grow0 + rr];   // routed token rows, gathered
+                else row = (size_t)(t.grow0 + rr);
+                b_src[q] = t.B + row * t.ldb + (lp ^ sw(r)) * EPC;
+            }
         }
         a_k = 0;
         b_k = 0;
@@ -451,6 +529,10 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         a_seg_step = (size_t)t.N * t.seg;
         seg_ld = t.seg;
         rows_valid_ld = t.rows_valid;
+        cnt_ld = t.cnt;
+        lda_ld = t.lda;
+        ldb_ld = t.ldb;
+        m0_ld = t.t0;
     };
     // Weight stage j is issued SA stage boundaries ahead of its use, token stage
     // j SB ahead (tokens first within a boundary).  A wave's weight loads per
@@ -463,6 +545,27 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     // experts along K).
     auto issue_a = [&](auto S_) __attribute__((always_inline)) {
         uint8_t* __restrict__ dst = stage_a(S_);
+        if constexpr (AKN) {
+            const size_t off = (size_t)a_k * lda_ld;
+            if (MODE == kModeWgrad && a_k + BK > cnt_ld) {
+                // the stage that holds the tile's padding rows: rows past the
+                // count re-read its last row (B reads zeros there)
+#pragma unroll
+                for (int q = 0; q < A_PW; ++q) {
+                    const int r = RPIA * (wv + NW * q) + lane / CHA;
+                    const long long rel = a_k + r < cnt_ld ? a_k : cnt_ld - 1 - r;
+                    __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + rel * lda_ld),
+                                                     (lds_void_t*)(dst + (wv + NW * q) * 1024), 16, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < A_PW; ++q)
+                    __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[q] + off),
+                                                     (lds_void_t*)(dst + (wv + NW * q) * 1024), 16, 0, 0);
+            }
+            a_k += BK;
+            return;
+        }
         const size_t aoff = a_seg + a_k;
 #pragma unroll
         for (int q = 0; q < A_PW; ++q)
@@ -476,6 +579,31 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     };
     auto issue_b = [&](auto S_) __attribute__((always_inline)) {
         uint8_t* __restrict__ dst = stage_b(S_);
+        if constexpr (BKN) {
+            const size_t off = (size_t)b_k * ldb_ld;
+            if (b_k + BK > cnt_ld) {
+                // rows past the tile's count read the zero row (same columns)
+#pragma unroll
+                for (int q = 0; q < B_PW; ++q) {
+                    const int qi = wv + NW * q;
+                    const int r = RPIB * qi + lane / CHB;
+                    const int m = min(m0_ld + ((lane % CHB) ^ swk(r)) * EPC, a.wg_M - EPC);
+                    const TE* src = b_k + r < cnt_ld ? b_src[q] + off : reinterpret_cast<const TE*>(a.zero) + m;
+                    if (qi < B_INS)
+                        __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(dst + qi * 1024), 16, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < B_PW; ++q) {
+                    const int qi = wv + NW * q;
+                    if (qi < B_INS)
+                        __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[q] + off), (lds_void_t*)(dst + qi * 1024),
+                                                         16, 0, 0);
+                }
+            }
+            b_k += BK;
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < B_PW; ++q) {
             const int qi = wv + NW * q;
@@ -540,6 +668,43 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     constexpr int A_STEP = 16 * ROWB;               // bytes between a wave's weight-row blocks
     constexpr int B_STEP = 16 * WM * ROWB;          // bytes between a wave's token blocks
 
+    // [K][N] stages, bf16: lane l of 16-lane group g = l/16 addresses K row
+    // 8g + (l/4)%4 (+ 32 per k-step, + 4 for the second read) at columns
+    // 4(l%4).. of its 16-column block; swk of all those rows is the same.
+    // The chunk of fragment i (A) is ((wn0 + 16i)/8 + (l%4)/2) ^ sz, whose
+    // bits 1-2 (2i, i < 4) meet sz there: its byte offset is a lane constant
+    // XOR 32i.  For B, chunk (16(WM j + wm))/8 + (l%4)/2 = 4j + 2wm + ..:
+    // a lane constant XOR 64j.
+    int a_kn0 = 0, b_kn0 = 0;
+    if constexpr (sizeof(TE) == 2 && (AKN || BKN)) {
+        static_assert(!AKN || (FN <= 4 && WTN % 64 == 0), "A fragment offsets: 2i in chunk bits 1-2");
+        static_assert(!BKN || (WM == 2 && FM <= 8), "B fragment offsets: 4j in chunk bits 2-4");
+        const int g = lane >> 4, j4 = (lane >> 2) & 3, q4 = lane & 3;
+        const int sz = (j4 | ((g & 1) << 2)) << 1;
+        a_kn0 = (8 * g + j4) * RBA + ((((wn0 >> 3) + (q4 >> 1)) ^ sz) << 4) + (q4 & 1) * 8;
+        b_kn0 = (8 * g + j4) * RBB + (((2 * wm + (q4 >> 1)) ^ sz) << 4) + (q4 & 1) * 8;
+    }
+    // [K][N] stages, fp32: element k = 16 ks + 4(l/16) + c of column cb + l%16
+    // for c < 4 (the K order of the K-major fragments)
+    auto read_kn32 = [&](const uint8_t* __restrict__ st, int ks, int cb, int rb) __attribute__((always_inline)) {
+        float v[4];
+        const uint8_t* p = st + (4 * (lane >> 4)) * rb + (cb + (lane & 15)) * 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const float*>(p + (16 * ks + c) * rb);
+        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    };
+    // fragment i (A: weight rows wn0 + 16i..) / j (B: token block WM*j + wm) of k-step ks
+    auto read_a = [&](const uint8_t* __restrict__ st, int ks, int i) __attribute__((always_inline)) -> uint4 {
+        if constexpr (!AKN) return *reinterpret_cast<const uint4*>(st + a_rd[ks] + i * A_STEP);
+        else if constexpr (sizeof(TE) == 2) return read_tr16_frag(st + (a_kn0 ^ (32 * i)) + ks * 32 * RBA, RBA);
+        else return read_kn32(st, ks, wn0 + 16 * i, RBA);
+    };
+    auto read_b = [&](const uint8_t* __restrict__ st, int ks, int j) __attribute__((always_inline)) -> uint4 {
+        if constexpr (!BKN) return *reinterpret_cast<const uint4*>(st + b_rd[ks] + j * B_STEP);
+        else if constexpr (sizeof(TE) == 2) return read_tr16_frag(st + (b_kn0 ^ (64 * j)) + ks * 32 * RBB, RBB);
+        else return read_kn32(st, ks, 16 * (WM * j + wm), RBB);
+    };
+
     // Tile-round rendezvous of an XCD (SYNC): every workgroup counts each tile
     // it finishes on its XCD's counter and waits, for at most kSpinLimit polls,
     // until every workgroup of its round has finished, so that the workgroups
@@ -583,9 +748,9 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
             const uint8_t* __restrict__ s0a = stage_a(std::integral_constant<int, 0>{});
             const uint8_t* __restrict__ s0b = stage_b(std::integral_constant<int, 0>{});
 #pragma unroll
-            for (int i = 0; i < FN; ++i) fa[0][i] = *reinterpret_cast<const uint4*>(s0a + a_rd[0] + i * A_STEP);
+            for (int i = 0; i < FN; ++i) fa[0][i] = read_a(s0a, 0, i);
 #pragma unroll
-            for (int j = 0; j < H1; ++j) fb[0][j] = *reinterpret_cast<const uint4*>(s0b + b_rd[0] + j * B_STEP);
+            for (int j = 0; j < H1; ++j) fb[0][j] = read_b(s0b, 0, j);
         }
         for (int kt0 = 0; kt0 < nk; kt0 += U) {
             static_for<0, U>([&](auto S_) __attribute__((always_inline)) {
@@ -608,13 +773,11 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
                             constexpr int halfn = H2 > 0 ? (hn & 1) : 0;
                             if constexpr (halfn == 0) {
 #pragma unroll
-                                for (int i = 0; i < FN; ++i)
-                                    fa[acur ^ 1][i] = *reinterpret_cast<const uint4*>(sba + a_rd[ksn] + i * A_STEP);
+                                for (int i = 0; i < FN; ++i) fa[acur ^ 1][i] = read_a(sba, ksn, i);
                             }
                             constexpr int j0 = halfn ? H1 : 0, jn = halfn ? H2 : H1;
 #pragma unroll
-                            for (int j = 0; j < jn; ++j)
-                                fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(sbb + b_rd[ksn] + (j0 + j) * B_STEP);
+                            for (int j = 0; j < jn; ++j) fb[bcur ^ 1][j] = read_b(sbb, ksn, j0 + j);
                         } else {
                             if (kt + 1 < nk) {
                                 // all reads of this stage are done: wait for stage kt+1
@@ -630,11 +793,9 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
                                 const uint8_t* __restrict__ snb = stage_b(std::integral_constant<int, snext>{});
                                 constexpr int an = (snext * KS) & 1;     // A buffer of the next stage's k-step 0
 #pragma unroll
-                                for (int i = 0; i < FN; ++i)
-                                    fa[an][i] = *reinterpret_cast<const uint4*>(sna + a_rd[0] + i * A_STEP);
+                                for (int i = 0; i < FN; ++i) fa[an][i] = read_a(sna, 0, i);
 #pragma unroll
-                                for (int j = 0; j < H1; ++j)
-                                    fb[bcur ^ 1][j] = *reinterpret_cast<const uint4*>(snb + b_rd[0] + j * B_STEP);
+                                for (int j = 0; j < H1; ++j) fb[bcur ^ 1][j] = read_b(snb, 0, j);
                             }
                         }
                         __builtin_amdgcn_sched_barrier(0);
@@ -868,10 +1029,11 @@ hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t s
     grid = (grid + 7) / 8 * 8;
     constexpr int kSync = MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kPrefillSyncGateUp
                           : MODE == kModeDown ? kPrefillSyncDown : 0;
-    if (cfg == 0 || MODE == kModeWgrad)
+    // the backward modes run the 256 x 256 tiles only
+    if (cfg == 0 || MODE == kModeWgrad || a_kn<MODE>())
         hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB, kPrefillRowB, 4,
                                            kSync, MODE>), dim3(grid), dim3(512), 0, stream, a);
-    else if constexpr (MODE != kModeWgrad)
+    else if constexpr (!a_kn<MODE>())
         hipLaunchKernelGGL((moe_gemm_kernel<TE, kDecodeBN, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, 0, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     return hipGetLastError();
@@ -1007,14 +1169,18 @@ hipError_t launch_dact(const MoeGemmParams& p, const BwdActBufs& b, hipStream_t 
     GemmKArgs a = base_args(p);
     const int bm = gemm_cfg_bm(p.cfg);
     a.round_counter = p.round_counters + 16;
-    a.A_routed = b.wdT;        // [E][I][H]
+    a.A_routed = p.w_d;        // [E][H][I]: K = H rows of I
+    a.lda_r = p.I;
     a.B_routed = b.dout;       // token rows gathered
     a.out_routed = b.dh_r;
     a.K_r = p.H;
     a.N_r = p.I;
     a.ntn_r = (a.N_r + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
     a.has_routed = p.has_routed;
-    a.A_shared = b.wshdT;      // [S*I][H]
+    a.A_shared = p.wsh_d;      // [S][H][I]: column s*I + i is column i of expert s
+    a.lda_s = p.I;
+    a.a_segn_s = p.I;
+    a.a_segstride_s = (long long)p.H * p.I;
     a.B_shared = b.dout;
     a.out_shared = b.dh_sh;
     a.K_s = p.H;
@@ -1033,6 +1199,38 @@ hipError_t launch_dact(const MoeGemmParams& p, const BwdActBufs& b, hipStream_t 
                                       stream);
 }
 
+hipError_t launch_dx(const MoeGemmParams& p, const void* dh_r, const void* dh_sh, void* dx_r, void* dx_sh,
+                     hipStream_t stream) {
+    GemmKArgs a = base_args(p);
+    const int bm = gemm_cfg_bm(p.cfg);
+    a.round_counter = p.round_counters + 8;
+    a.A_routed = p.w_gu;       // [E][2I][H]: K = 2I rows of H
+    a.lda_r = p.H;
+    a.B_routed = dh_r;         // [T*k][2I] sorted rows
+    a.out_routed = dx_r;       // [T*k][H] fp32, slot rows
+    a.K_r = 2 * p.I;
+    a.N_r = p.H;
+    a.ntn_r = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
+    a.has_routed = p.has_routed;
+    // shared experts: dh_sh [T][S*2I] against [S*2I][H], the S gate_up
+    // projections stacked along K, so the sum over shared experts happens
+    // inside the reduction
+    a.A_shared = p.wsh_gu;
+    a.lda_s = p.H;
+    a.a_segn_s = p.H;
+    a.a_segstride_s = 0;
+    a.B_shared = dh_sh;
+    a.out_shared = dx_sh;      // [T][H] fp32
+    a.K_s = 2 * p.S * p.I;
+    a.N_s = p.H;
+    a.ntn_s = a.ntn_r;
+    a.seg_s = a.K_s;
+    a.shared_mtiles = (p.T + bm - 1) / bm;
+    a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
+    return launch_dispatch<kModeDx>(p, a, a.shared_blocks + (p.has_routed ? p.max_routed_tiles * a.ntn_r : 0),
+                                    stream);
+}
+
 hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream) {
     GemmKArgs a = {};
     a.A_routed = w.A_r;
@@ -1040,8 +1238,13 @@ hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream) {
     a.A_shared = w.A_s;
     a.B_shared = w.B_s;
     a.poff = w.poff;
-    a.ld_r = w.ld_r;
-    a.ld_s = w.ld_s;
+    a.offsets = w.offsets;
+    a.zero = w.zero;
+    a.lda_r = w.lda_r;
+    a.ldb_r = w.ldb_r;
+    a.lda_s = w.lda_s;
+    a.ldb_s = w.ldb_s;
+    a.T = w.T;
     a.K_s = w.K_s;
     a.K_r = 1;
     a.a_sh_stride = w.a_sh_stride;

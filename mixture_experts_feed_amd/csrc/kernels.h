@@ -71,8 +71,6 @@ hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream);
 // h = gate_up(x) (no SwiGLU, fp32) for routed rows [T*k][2I] and shared [T][S*2I]
 hipError_t launch_gate_up_raw(const MoeGemmParams& p, void* h_r, void* h_sh, hipStream_t stream);
 struct BwdActBufs {
-    const void* wdT;     // [E][I][H] routed down projections, transposed
-    const void* wshdT;   // [S*I][H]  shared down projections, transposed
     const void* dout;    // [T][H]
     const void* h_r;     // [T*k][2I] fp32
     const void* h_sh;    // [T][S*2I] fp32
@@ -83,19 +81,30 @@ struct BwdActBufs {
     float* dgp_r;        // [T*k][I/64]
     float* dgp_sh;       // [T][S*I/64]
 };
-// dact = down^T dout per routed row / shared token, then the SwiGLU backward:
-// dh, a and partial routing-weight gradients (round counters 16..23)
+// dact = down^T dout per routed row / shared token (the down weights read in
+// their stored layout), then the SwiGLU backward: dh, a and partial
+// routing-weight gradients (round counters 16..23)
 hipError_t launch_dact(const MoeGemmParams& p, const BwdActBufs& b, hipStream_t stream);
-// out_p[m][n] = sum_k B_p[m][k] A_p[n][k] for problems p < E (routed: K and
-// the column offset from poff) and S shared ones (K = K_s)
+// dx rows = gate_up^T dh: routed dh_r -> dx_r [T*k][H] fp32 (slot rows),
+// shared dh_sh [T][S*2I] -> dx_sh [T][H] fp32; the gate_up weights read in
+// their stored layout (round counters 8..15)
+hipError_t launch_dx(const MoeGemmParams& p, const void* dh_r, const void* dh_sh, void* dx_r, void* dx_sh,
+                     hipStream_t stream);
+// out_p[m][n] = sum_k B_p[k][m] A_p[k][n] over K rows of the operands for
+// problems p < E (routed: rows offsets[p] .. offsets[p+1] of A_r and B_r, K
+// padded to poff[p+1] - poff[p] with zero rows of B) and S shared ones (K_s
+// rows, the first T of them real; shared problem s at element offsets
+// s*a_sh_stride of A_s and s*b_sh_stride of B_s)
 struct WgradParams {
-    int dtype, E, S, M, N;
+    int dtype, E, S, M, N, T;
     const void* A_r;
     const void* B_r;
     const void* A_s;
     const void* B_s;
     const int32_t* poff;
-    int ld_r, ld_s, K_s;
+    const int32_t* offsets;
+    const void* zero;   // max(M) zeros of the operand type
+    int lda_r, ldb_r, lda_s, ldb_s, K_s;
     long long a_sh_stride, b_sh_stride;
     float* out_r;
     float* out_s;
@@ -103,13 +112,14 @@ struct WgradParams {
 hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream);
 
 // ---- backward, other kernels (backward.hip) --------------------------------
-// out_b[d][c] = src_b[row(c)][d]; row(c) = map[c] (-1: zero) or c (< n_rows)
-hipError_t launch_gather_transpose(int dtype, const void* src, void* out, const int32_t* map, int n_rows, int C,
-                                   int D, int batch, long long src_batch, long long out_batch, hipStream_t stream);
-// poff [E+1]: experts' row counts rounded up to 64, prefix-summed; for padded
-// columns c < C the sorted row (or -1) and its token (or -1)
-hipError_t launch_column_map(const int32_t* counts, const int32_t* offsets, const int32_t* row_token, int E, int C,
-                             int32_t* poff, int32_t* col_row, int32_t* col_tok, hipStream_t stream);
+// out[r] = src[row_token[r]] (rows of D elements) for the sorted rows r <
+// offsets[E] (at most max_rows)
+hipError_t launch_gather_rows(int dtype, const void* src, const int32_t* row_token, const int32_t* offsets, int E,
+                              int max_rows, int D, void* out, hipStream_t stream);
+// poff [E+1]: experts' row counts rounded up to 64, prefix-summed
+hipError_t launch_padded_offsets(const int32_t* counts, int E, int32_t* poff, hipStream_t stream);
+// n 32-bit words of zeros (a kernel, so that the call can be graph-captured)
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_router_backward(const double* zpart, int ksplit, const int32_t* topk_idx, const int32_t* pos,
                                   const float* dgp_r, const float* dgp_sh, int T, int E, int S, int k, int I,
                                   float route_scale, float global_scale, float* dz, float* dzc, hipStream_t stream);
