@@ -20,10 +20,16 @@ namespace inkling {
 
 namespace {
 
-constexpr int kTokTile = 32;   // tokens per workgroup (2 blocks of 16)
 constexpr int kExpTile = 48;   // logits columns per workgroup (3 blocks of 16)
 constexpr int kKChunk = 64;    // hidden-dim chunk staged in LDS (two buffers)
-constexpr int kRouterThreads = 64 * (kTokTile / 16) * (kExpTile / 16);   // one wave per 16x16 block
+// Token tiles: 128 tokens, 12 waves (three per SIMD, so that every SIMD carries
+// the same MFMA work), each wave two 16-token blocks sharing one widened bank
+// fragment; below kBigTileTokens tokens, 32 tokens and 6 waves of one block,
+// which waste fewer MFMAs on empty rows.
+constexpr int kBigTileTokens = 2048;
+int router_tok_tile(int T) { return T >= kBigTileTokens ? 128 : 32; }
+template <int TOK, int WTOK>
+constexpr int router_threads() { return 64 * (TOK / 16 / WTOK) * (kExpTile / 16); }
 
 // kRowVals consecutive values of a row, kept as raw 16-byte words
 constexpr int kRowVals = 16;
@@ -58,31 +64,35 @@ __device__ __forceinline__ double widen(bf16_t v) { return (double)__uint_as_flo
 __device__ __forceinline__ double widen(float v) { return (double)v; }
 
 // zpart[ks][t][e] = sum over h in slice ks of x[t][h] * bank[e][h], in fp64.
-// grid (ceil(T/32), ceil(NE/48), ksplit), 6 waves: wave w owns the 16x16 block
-// (tokens 16*(w%2).., bank rows 16*(w/2)..) of the tile.  Operands are staged
-// in LDS in their own precision and widened to fp64 (exactly) as the MFMA
-// fragments are read; the next chunk's global loads are in flight while the
-// current one is multiplied.
-template <typename TX>
-__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const TX* __restrict__ x,
+// grid (ceil(T/TOK), ceil(NE/48), ksplit); wave w owns the WTOK 16x16 blocks of
+// tokens 16*WTOK*(w % nw).. against bank rows 16*(w / nw).. of the tile (nw =
+// TOK/16/WTOK).  Operands are staged in LDS in their own precision and widened
+// to fp64 (exactly) as the MFMA fragments are read; the next chunk's global
+// loads are in flight while the current one is multiplied.
+template <typename TX, int TOK, int WTOK>
+__global__ __launch_bounds__((router_threads<TOK, WTOK>())) void router_logits_kernel(const TX* __restrict__ x,
                                                                        const float* __restrict__ bank,
                                                                        double* __restrict__ zpart, int T, int H,
                                                                        int NE, int klen) {
     // [buffer][16-row block][k][row in block]: an MFMA operand fragment (lane l
     // holds row l%16 at k = l/16) is one contiguous run of 64 elements
+    constexpr int kTokTile = TOK, kWaveTok = WTOK, kTokWaves = TOK / 16 / WTOK;
+    constexpr int kRouterThreads = router_threads<TOK, WTOK>();
     __shared__ TX xs[2][kTokTile / 16][kKChunk][16];
     __shared__ float gs[2][kExpTile / 16][kKChunk][16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int t0 = blockIdx.x * kTokTile, e0 = blockIdx.y * kExpTile, ks = blockIdx.z;
     const int kbeg = ks * klen;
     const int nchunks = min(klen, H - kbeg) / kKChunk;
-    const int tb = wv & 1, eb = wv >> 1;   // this wave's token / bank-row block
-    // kChains accumulators (k-steps taken round-robin) so consecutive MFMAs of a
-    // wave are independent
+    const int tb = (wv % kTokWaves) * kWaveTok, eb = wv / kTokWaves;   // first token block, bank-row block
+    // kChains accumulators per token block (k-steps taken round-robin) so
+    // consecutive MFMAs of a wave are independent
     constexpr int kChains = 4;
-    f64x4_t acc[kChains];
+    f64x4_t acc[kWaveTok][kChains];
 #pragma unroll
-    for (int i = 0; i < kChains; ++i) acc[i] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int u = 0; u < kWaveTok; ++u)
+#pragma unroll
+        for (int i = 0; i < kChains; ++i) acc[u][i] = f64x4_t{0.0, 0.0, 0.0, 0.0};
     // staging: threads [0, 128) load kRowVals hidden values of one token row,
     // threads [128, 320) kRowVals bank values of one bank row
     constexpr int kPerRow = kKChunk / kRowVals;   // threads per row
@@ -122,14 +132,18 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const TX*
 #pragma unroll
         for (int kk = 0; kk < kKChunk; kk += 4 * kChains) {
             // A (16 tokens x 4): lane holds A[lane%16][lane/16]; B (4 x 16 bank rows): B[lane/16][lane%16]
-            double a[kChains], b[kChains];
+            double a[kWaveTok][kChains], b[kChains];
 #pragma unroll
             for (int i = 0; i < kChains; ++i) {
-                a[i] = widen(xs[buf][tb][kk + 4 * i + (lane >> 4)][lane & 15]);
                 b[i] = widen(gs[buf][eb][kk + 4 * i + (lane >> 4)][lane & 15]);
+#pragma unroll
+                for (int u = 0; u < kWaveTok; ++u) a[u][i] = widen(xs[buf][tb + u][kk + 4 * i + (lane >> 4)][lane & 15]);
             }
 #pragma unroll
-            for (int i = 0; i < kChains; ++i) acc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[i], acc[i], 0, 0, 0);
+            for (int i = 0; i < kChains; ++i)
+#pragma unroll
+                for (int u = 0; u < kWaveTok; ++u)
+                    acc[u][i] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[u][i], b[i], acc[u][i], 0, 0, 0);
         }
     };
     gload(vx0, vg0, 0);
@@ -143,10 +157,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const TX*
     // rows are 4*(lane/16) + r).
     const int eo = e0 + eb * 16 + (lane & 15);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int to = t0 + tb * 16 + (lane >> 4) + 4 * r;
-        if (to < T && eo < NE) zpart[((size_t)ks * T + to) * NE + eo] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
-    }
+    for (int u = 0; u < kWaveTok; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int to = t0 + (tb + u) * 16 + (lane >> 4) + 4 * r;
+            if (to < T && eo < NE)
+                zpart[((size_t)ks * T + to) * NE + eo] = (acc[u][0][r] + acc[u][1][r]) + (acc[u][2][r] + acc[u][3][r]);
+        }
 }
 
 constexpr int kMaxPerLane = 8;  // experts per lane: n_routed + n_shared <= 512
@@ -256,7 +273,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double* __rest
 }  // namespace
 
 int router_ksplit(int T, int H, int NE) {
-    const int tiles = ((T + kTokTile - 1) / kTokTile) * ((NE + kExpTile - 1) / kExpTile);
+    const int tok = router_tok_tile(T);
+    const int tiles = ((T + tok - 1) / tok) * ((NE + kExpTile - 1) / kExpTile);
     int ks = 1;
     // split the hidden dim until ~3 workgroups per CU exist (768), keeping >= 256 per slice
     while (tiles * ks * 2 <= 768 && (H / (ks * 2)) >= 256 && (H % (ks * 2 * kKChunk)) == 0) ks *= 2;
@@ -265,14 +283,26 @@ int router_ksplit(int T, int H, int NE) {
 
 hipError_t launch_router_logits(int dtype, const void* x, const float* bank, double* zpart, int T, int H, int NE,
                                 int ksplit, hipStream_t stream) {
-    dim3 grid((T + kTokTile - 1) / kTokTile, (NE + kExpTile - 1) / kExpTile, ksplit);
+    const int tok = router_tok_tile(T);
+    dim3 grid((T + tok - 1) / tok, (NE + kExpTile - 1) / kExpTile, ksplit);
     const int klen = H / ksplit;
-    if (dtype == 1)
-        hipLaunchKernelGGL(router_logits_kernel<bf16_t>, grid, dim3(kRouterThreads), 0, stream, (const bf16_t*)x, bank,
-                           zpart, T, H, NE, klen);
-    else
-        hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(kRouterThreads), 0, stream, (const float*)x, bank,
-                           zpart, T, H, NE, klen);
+    if (tok == 128) {
+        constexpr int threads = router_threads<128, 2>();
+        if (dtype == 1)
+            hipLaunchKernelGGL((router_logits_kernel<bf16_t, 128, 2>), grid, dim3(threads), 0, stream,
+                               (const bf16_t*)x, bank, zpart, T, H, NE, klen);
+        else
+            hipLaunchKernelGGL((router_logits_kernel<float, 128, 2>), grid, dim3(threads), 0, stream,
+                               (const float*)x, bank, zpart, T, H, NE, klen);
+    } else {
+        constexpr int threads = router_threads<32, 1>();
+        if (dtype == 1)
+            hipLaunchKernelGGL((router_logits_kernel<bf16_t, 32, 1>), grid, dim3(threads), 0, stream,
+                               (const bf16_t*)x, bank, zpart, T, H, NE, klen);
+        else
+            hipLaunchKernelGGL((router_logits_kernel<float, 32, 1>), grid, dim3(threads), 0, stream,
+                               (const float*)x, bank, zpart, T, H, NE, klen);
+    }
     return hipGetLastError();
 }
 

@@ -90,6 +90,11 @@ EDGE = {
                                           route_scale=8.0),
     "single_token": wl.custom(T=1, hidden=128, n_routed=8, top_k=2, n_shared=1, intermediate=64),
     "minimal_width_h64_i64": wl.custom(T=90, hidden=64, n_routed=6, top_k=3, n_shared=3, intermediate=64),
+    # from 2048 tokens the gate logits run on 128-token tiles: a ragged last tile
+    "ragged_big_router_tile_bf16": wl.custom(T=2500, hidden=256, n_routed=16, top_k=4, n_shared=1,
+                                             intermediate=128),
+    "ragged_big_router_tile_f32": wl.custom(T=2100, hidden=128, n_routed=8, top_k=2, n_shared=1, intermediate=64,
+                                            dtype="f32"),
 }
 
 
