@@ -130,13 +130,20 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
                                  rb.topk_idx, rb.topk_w, rb.shared_g, s));
     HIP_TRY(mark(2, s));
     if (!permute) return INKLING_OK;
-    uint64_t* masks = at<uint64_t>(ws, L.masks);
-    int32_t* prefix = at<int32_t>(ws, L.prefix);
-    HIP_TRY(launch_build_masks(rb.topk_idx, pad, T, E, k, masks, L.W, s));
-    HIP_TRY(launch_scan(masks, L.W, E, prefix, rb.counts, rb.offsets, rb.tiles ? L.bm : 0, rb.tiles, rb.num_tiles,
-                        rb.tiles ? at<int32_t>(ws, L.round_counters) : nullptr, s));
-    HIP_TRY(launch_scatter(rb.topk_idx, rb.topk_w, pad, masks, prefix, rb.offsets, T, E, k, L.W, rb.sorted_slots,
-                           rb.row_token, rb.row_gamma, rb.pos, s));
+    int32_t* rc = rb.tiles ? at<int32_t>(ws, L.round_counters) : nullptr;
+    if (L.W == 1) {
+        HIP_TRY(launch_permute_small(rb.topk_idx, rb.topk_w, pad, T, E, k, rb.tiles ? L.bm : 0, rb.counts, rb.offsets,
+                                     rb.tiles, rb.num_tiles, rc, rb.sorted_slots, rb.row_token, rb.row_gamma, rb.pos,
+                                     s));
+    } else {
+        uint64_t* masks = at<uint64_t>(ws, L.masks);
+        int32_t* prefix = at<int32_t>(ws, L.prefix);
+        HIP_TRY(launch_build_masks(rb.topk_idx, pad, T, E, k, masks, L.W, s));
+        HIP_TRY(launch_scan(masks, L.W, E, prefix, rb.counts, rb.offsets, rb.tiles ? L.bm : 0, rb.tiles, rb.num_tiles,
+                            rc, s));
+        HIP_TRY(launch_scatter(rb.topk_idx, rb.topk_w, pad, masks, prefix, rb.offsets, T, E, k, L.W, rb.sorted_slots,
+                               rb.row_token, rb.row_gamma, rb.pos, s));
+    }
     HIP_TRY(mark(3, s));
     return INKLING_OK;
 }

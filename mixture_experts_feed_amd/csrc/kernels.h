@@ -30,6 +30,11 @@ hipError_t launch_scatter(const int32_t* topk_idx, const float* topk_w, const ui
                           const int32_t* prefix, const int32_t* offsets, int T, int E, int k, int W,
                           int32_t* sorted_slots, int32_t* row_token, float* row_gamma, int32_t* pos,
                           hipStream_t stream);
+// T <= 64: the three steps above in one launch (same outputs)
+hipError_t launch_permute_small(const int32_t* topk_idx, const float* topk_w, const uint8_t* pad, int T, int E, int k,
+                                int bm, int32_t* counts, int32_t* offsets, RoutedTile* tiles, int32_t* num_tiles,
+                                int32_t* round_counters, int32_t* sorted_slots, int32_t* row_token, float* row_gamma,
+                                int32_t* pos, hipStream_t stream);
 
 // ---- grouped GEMMs and combine (gemm.hip) ---------------------------------
 struct MoeGemmParams {

@@ -136,7 +136,93 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
     }
 }
 
+// T <= 64 (a single mask word): the mask, scan and scatter steps above in one
+// workgroup, with the masks in LDS and every prefix zero.
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, const uint8_t* __restrict__ pad, int T,
+    int E, int k, int bm, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, RoutedTile* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles, int32_t* __restrict__ round_counters, int32_t* __restrict__ sorted_slots,
+    int32_t* __restrict__ row_token, float* __restrict__ row_gamma, int32_t* __restrict__ pos) {
+    __shared__ unsigned long long m[kMaxExperts];
+    __shared__ int32_t off[kMaxExperts + 1];
+    __shared__ int32_t tstart[kMaxExperts + 1];
+    const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+    const int n_slots = T * k;
+    if (round_counters != nullptr && tid < kRoundCounters) round_counters[tid] = 0;
+    for (int e = tid; e < E; e += blockDim.x) m[e] = 0ull;
+    __syncthreads();
+    for (int sl = tid; sl < n_slots; sl += blockDim.x) {
+        const int t = sl / k;
+        if (pad == nullptr || pad[t] == 0) atomicOr(&m[topk_idx[sl]], 1ull << t);
+    }
+    __syncthreads();
+    if (wv == 0) {
+        // exclusive scans over experts of the counts and of the row-tile counts
+        int carry = 0, tcarry = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int e = base + lane;
+            const int c = e < E ? __popcll(m[e]) : 0;
+            const int tc = (e < E && bm > 0) ? (c + bm - 1) / bm : 0;
+            int incl = c, tincl = tc;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int o = __shfl_up(incl, d);
+                const int to = __shfl_up(tincl, d);
+                if (lane >= d) {
+                    incl += o;
+                    tincl += to;
+                }
+            }
+            if (e < E) {
+                off[e] = carry + incl - c;
+                tstart[e] = tcarry + tincl - tc;
+            }
+            carry += __shfl(incl, 63);
+            tcarry += __shfl(tincl, 63);
+        }
+        if (lane == 0) {
+            off[E] = carry;
+            tstart[E] = tcarry;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += blockDim.x) {
+        offsets[e] = off[e];
+        if (e < E && counts != nullptr) counts[e] = __popcll(m[e]);
+    }
+    if (tiles != nullptr) {
+        for (int e = tid; e < E; e += blockDim.x) {
+            const int n = tstart[e + 1] - tstart[e];
+            for (int j = 0; j < n; ++j) tiles[tstart[e] + j] = RoutedTile{e, j * bm};
+        }
+        if (tid == 0) *num_tiles = tstart[E];
+    }
+    for (int sl = tid; sl < n_slots; sl += blockDim.x) {
+        const int t = sl / k;
+        if (pad != nullptr && pad[t] != 0) {
+            if (pos) pos[sl] = -1;
+            continue;
+        }
+        const int e = topk_idx[sl];
+        const uint64_t below = (t == 0) ? 0ull : (~0ull >> (64 - t));
+        const int row = off[e] + __popcll(m[e] & below);
+        if (sorted_slots) sorted_slots[row] = sl;
+        if (row_token) row_token[row] = t;
+        if (row_gamma) row_gamma[row] = topk_w[sl];
+        if (pos) pos[sl] = row;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_permute_small(const int32_t* topk_idx, const float* topk_w, const uint8_t* pad, int T, int E, int k,
+                                int bm, int32_t* counts, int32_t* offsets, RoutedTile* tiles, int32_t* num_tiles,
+                                int32_t* round_counters, int32_t* sorted_slots, int32_t* row_token, float* row_gamma,
+                                int32_t* pos, hipStream_t stream) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, stream, topk_idx, topk_w, pad, T, E, k, bm, counts,
+                       offsets, tiles, num_tiles, round_counters, sorted_slots, row_token, row_gamma, pos);
+    return hipGetLastError();
+}
 
 hipError_t launch_build_masks(const int32_t* topk_idx, const uint8_t* pad, int T, int E, int k, uint64_t* masks,
                               int W, hipStream_t stream) {

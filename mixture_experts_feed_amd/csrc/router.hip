@@ -167,13 +167,16 @@ __global__ __launch_bounds__((router_threads<TOK, WTOK>())) void router_logits_k
 }
 
 constexpr int kMaxPerLane = 8;  // experts per lane: n_routed + n_shared <= 512
+constexpr int kFewPerLane = 3;  // n_routed + n_shared <= 192
 
 __device__ __forceinline__ double log_sigmoid(double z) {
     // log sigma(z) = -log(1 + e^-z), evaluated on the side that cannot overflow
     return z >= 0.0 ? -log1p(exp(-z)) : z - log1p(exp(z));
 }
 
-// One wave per token.  Lane j holds logits of experts j, j+64, ... .
+// One wave per token.  Lane j holds logits of experts j, j+64, ... (PL of them);
+// the partial logits of BATCH hidden-dim slices are loaded together.
+template <int PL, int BATCH>
 __global__ __launch_bounds__(256) void router_select_kernel(const double* __restrict__ zpart, int ksplit,
                                                             const float* __restrict__ bias, int T, int E, int S,
                                                             int k, double scale, int32_t* __restrict__ topk_idx,
@@ -184,30 +187,30 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double* __rest
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;  // wave-uniform; no block-level barrier below
     const int NE = E + S;
-    double sc[kMaxPerLane];
-    bool live[kMaxPerLane];
-    // logits: sum of the hidden-dim slices in slice order; the loads of four
-    // slices for all of the lane's experts are issued together
-    double z[kMaxPerLane];
+    double sc[PL];
+    bool live[PL];
+    // logits: sum of the hidden-dim slices in slice order
+    constexpr int kBatch = BATCH;
+    double z[PL];
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) z[j] = 0.0;
-    for (int s0 = 0; s0 < ksplit; s0 += 4) {
-        double p[4][kMaxPerLane];
+    for (int j = 0; j < PL; ++j) z[j] = 0.0;
+    for (int s0 = 0; s0 < ksplit; s0 += kBatch) {
+        double p[kBatch][PL];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-            for (int j = 0; j < kMaxPerLane; ++j) {
+            for (int j = 0; j < PL; ++j) {
                 const int e = lane + 64 * j;
                 p[u][j] = (s0 + u < ksplit && e < NE) ? zpart[((size_t)(s0 + u) * T + t) * NE + e] : 0.0;
             }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-            for (int j = 0; j < kMaxPerLane; ++j)
+            for (int j = 0; j < PL; ++j)
                 if (s0 + u < ksplit) z[j] += p[u][j];
     }
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < PL; ++j) {
         const int e = lane + 64 * j;
         live[j] = false;
         sc[j] = 0.0;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double* __rest
         double bs = 0.0;
         int be = 0x7FFFFFFF;
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
+        for (int j = 0; j < PL; ++j) {
             const int e = lane + 64 * j;
             if (live[j] && (be == 0x7FFFFFFF || sc[j] > bs || (sc[j] == bs && e < be))) {
                 bs = sc[j];
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double* __rest
         // be is now wave-uniform
         if ((be & 63) == lane) {
 #pragma unroll
-            for (int j = 0; j < kMaxPerLane; ++j)
+            for (int j = 0; j < PL; ++j)
                 if (lane + 64 * j == be) live[j] = false;
         }
         if (lane == i) my_sel = be;
@@ -310,8 +313,21 @@ hipError_t launch_router_select(const double* zpart, int ksplit, const float* bi
                                 float route_scale, float global_scale, int32_t* topk_idx, float* topk_w,
                                 float* shared_g, hipStream_t stream) {
     const double scale = (double)route_scale * (double)global_scale;
-    hipLaunchKernelGGL(router_select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, zpart, ksplit, bias, T, E, S, k,
-                       scale, topk_idx, topk_w, shared_g);
+    // few experts per lane and many slices (the few-token splits): every
+    // slice's loads at once; otherwise four slices at a time
+    const dim3 grid((T + 3) / 4);
+    if (E + S <= 64 * kFewPerLane && ksplit > 8)
+        hipLaunchKernelGGL((router_select_kernel<kFewPerLane, 16>), grid, dim3(256), 0, stream, zpart, ksplit, bias, T,
+                           E, S, k, scale, topk_idx, topk_w, shared_g);
+    else if (E + S <= 64 * kFewPerLane && ksplit > 4)
+        hipLaunchKernelGGL((router_select_kernel<kFewPerLane, 8>), grid, dim3(256), 0, stream, zpart, ksplit, bias, T,
+                           E, S, k, scale, topk_idx, topk_w, shared_g);
+    else if (E + S <= 64 * kFewPerLane)
+        hipLaunchKernelGGL((router_select_kernel<kFewPerLane, 4>), grid, dim3(256), 0, stream, zpart, ksplit, bias, T,
+                           E, S, k, scale, topk_idx, topk_w, shared_g);
+    else
+        hipLaunchKernelGGL((router_select_kernel<kMaxPerLane, 4>), grid, dim3(256), 0, stream, zpart, ksplit, bias, T,
+                           E, S, k, scale, topk_idx, topk_w, shared_g);
     return hipGetLastError();
 }
 
