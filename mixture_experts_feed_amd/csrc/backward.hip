@@ -175,58 +175,56 @@ __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return __uint_as_flo
 template <>
 __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 
-constexpr int kBankRows = 16;   // bank rows per workgroup
-constexpr int kBankT = 64;      // tokens staged per step
-constexpr int kBankCols = 4;    // hidden columns per thread
-constexpr int kBankSplit = 8;   // token ranges summed separately, then in order
+constexpr int kBankSplit = 32;   // token ranges summed separately, then in order
+constexpr int kBankJW = 3;       // 16-row blocks of the bank per wave
 
-// part[ts][j][h] = sum over t in token range ts (ascending) of dz[t][j] * x[t][h];
-// grid (ceil(H/256), ceil(NE/16), kBankSplit), 64 threads x 4 columns.
+// part[ts][j][h] = sum over t in token range ts of dz[t][j] * x[t][h], on the
+// fp32 matrix cores (x widened exactly, products and sums in fp32); grid
+// (H/64, ceil(NE/(16*kBankJW)), kBankSplit), one wave of 48 bank rows x 64
+// hidden columns.  MFMA operands come straight from global memory: lane l
+// holds dz[t + l/16][j0 + l%16] (A, rows = bank rows) and x[t + l/16][h0 + l%16]
+// (B, columns = hidden), four tokens per step in ascending order.
 template <typename TX>
 __global__ __launch_bounds__(64) void dbank_partial_kernel(const float* __restrict__ dz, const TX* __restrict__ x,
                                                            int T, int H, int NE, float* __restrict__ part) {
-    __shared__ float zs[kBankT][kBankRows];
-    const int h0 = blockIdx.x * 64 * kBankCols + threadIdx.x * kBankCols;
-    const int j0 = blockIdx.y * kBankRows;
+    const int lane = threadIdx.x, kr = lane >> 4, cl = lane & 15;
+    const int h0 = blockIdx.x * 64, jb0 = blockIdx.y * kBankJW;
     const int tlen = (T + kBankSplit - 1) / kBankSplit;
     const int tb = blockIdx.z * tlen, te = min(T, tb + tlen);
-    float acc[kBankRows][kBankCols];
+    f32x4_t acc[kBankJW][4];
 #pragma unroll
-    for (int j = 0; j < kBankRows; ++j)
+    for (int u = 0; u < kBankJW; ++u)
 #pragma unroll
-        for (int c = 0; c < kBankCols; ++c) acc[j][c] = 0.f;
-    for (int t0 = tb; t0 < te; t0 += kBankT) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < kBankT * kBankRows; i += 64) {
-            const int tt = t0 + i / kBankRows, j = j0 + i % kBankRows;
-            zs[i / kBankRows][i % kBankRows] = (tt < te && j < NE) ? dz[(size_t)tt * NE + j] : 0.f;
+        for (int v = 0; v < 4; ++v) acc[u][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int t = tb; t < te; t += 4) {
+        const int tt = t + kr;
+        const bool tv = tt < te;
+        float a[kBankJW], b[4];
+#pragma unroll
+        for (int u = 0; u < kBankJW; ++u) {
+            const int j = (jb0 + u) * 16 + cl;
+            a[u] = (tv && j < NE) ? dz[(size_t)tt * NE + j] : 0.f;
         }
-        __syncthreads();
-        if (h0 < H) {
-            const int tn = min(kBankT, te - t0);
-            for (int tt = 0; tt < tn; ++tt) {
-                const TX* xr = x + (size_t)(t0 + tt) * H + h0;
-                float xv[kBankCols];
 #pragma unroll
-                for (int c = 0; c < kBankCols; ++c) xv[c] = to_f32<TX>(xr[c]);
+        for (int v = 0; v < 4; ++v) b[v] = tv ? to_f32<TX>(x[(size_t)tt * H + h0 + 16 * v + cl]) : 0.f;
 #pragma unroll
-                for (int j = 0; j < kBankRows; ++j) {
-                    const float z = zs[tt][j];
+        for (int u = 0; u < kBankJW; ++u)
 #pragma unroll
-                    for (int c = 0; c < kBankCols; ++c) acc[j][c] += z * xv[c];
-                }
+            for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[v], acc[u][v], 0, 0, 0);
+    }
+    // lane l holds rows j0 + 4(l/16) + r, column h0 + l%16 of each 16x16 block
+#pragma unroll
+    for (int u = 0; u < kBankJW; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = (jb0 + u) * 16 + 4 * kr + r;
+            if (j < NE) {
+                float* o = part + ((size_t)blockIdx.z * NE + j) * H + h0 + cl;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[16 * v] = acc[u][v][r];
             }
         }
-    }
-    if (h0 < H) {
-#pragma unroll
-        for (int j = 0; j < kBankRows; ++j)
-            if (j0 + j < NE) {
-                float* o = part + ((size_t)blockIdx.z * NE + j0 + j) * H + h0;
-#pragma unroll
-                for (int c = 0; c < kBankCols; ++c) o[c] = acc[j][c];
-            }
-    }
 }
 
 __global__ __launch_bounds__(256) void dbank_reduce_kernel(const float* __restrict__ part, int n, float* __restrict__ out) {
@@ -292,7 +290,7 @@ hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, 
 
 hipError_t launch_dbank(int dtype, const float* dz, const void* x, int T, int H, int NE, float* part, float* dbank,
                         hipStream_t stream) {
-    dim3 grid((H + 64 * kBankCols - 1) / (64 * kBankCols), (NE + kBankRows - 1) / kBankRows, kBankSplit);
+    dim3 grid(H / 64, (NE + 16 * kBankJW - 1) / (16 * kBankJW), kBankSplit);
     if (dtype == 1)
         hipLaunchKernelGGL(dbank_partial_kernel<bf16_t>, grid, dim3(64), 0, stream, dz, (const bf16_t*)x, T, H, NE,
                            part);
