@@ -373,7 +373,26 @@ def main():
                               "recompute_flops": re_flops,
                               "TFLOP_s_with_recompute": round((bw_flops + re_flops) / (bms * 1e-3) / 1e12, 2)}
         log(f"[bench] backward {bms:.3f} ms, {btf:.1f} TFLOP/s algorithmic")
-        del bws, grads, dout_b
+
+        # training step: the training forward keeps the gate_up projections,
+        # and the backward reads them instead of recomputing
+        saved = torch.empty(B.saved_size(bdims), dtype=torch.uint8, device=dev)
+        tr_out = torch.empty_like(inp["x"])
+
+        def train_call():
+            B.forward(inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"], inp["wsh_gu"], inp["wsh_d"],
+                      w.top_k, w.route_scale, w.global_scale, out=tr_out, workspace=ws, saved=saved)
+            B.backward(inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"], inp["wsh_gu"], inp["wsh_d"],
+                       w.top_k, w.route_scale, w.global_scale, dout_b, workspace=bws, grads=grads, saved=saved)
+
+        tms, _ = run_timed(torch, B, train_call, bw_steps, 2, events)
+        ttf = (w.flops_alg() + bw_flops) / (tms * 1e-3) / 1e12
+        result["train_step"] = {"workload": w.name, "ms_per_step": round(tms, 4), "TFLOP_s": round(ttf, 2),
+                                "frac_of_peak": round(ttf / PEAK_BF16_TFLOPS, 4),
+                                "saved_bytes": B.saved_size(bdims),
+                                "note": "inkling_moe_forward_train + inkling_moe_backward from the saved projections"}
+        log(f"[bench] training step (forward keeping h + backward) {tms:.3f} ms, {ttf:.1f} TFLOP/s algorithmic")
+        del bws, grads, dout_b, saved, tr_out
 
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_tokens} tokens")

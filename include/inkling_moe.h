@@ -144,14 +144,34 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
                         void* stream);
 
 /*
+ * Training forward: inkling_moe_forward (same out, bit for bit) that also
+ * keeps, for inkling_moe_backward, the gate_up projections h = gate_up(x) in
+ * fp32, the interleaved [gate, up] columns of each row:
+ *   saved = [T*top_k][2*I] for the routed rows, in the expert-sorted order of
+ *           the routing (rows past the routed count unused), then
+ *           [T][n_shared*2*I] for the shared experts;
+ * inkling_moe_saved_size gives its size in bytes.  The caller owns `saved`
+ * (device memory), and it stays valid for a backward with the same dims,
+ * inputs, gate, experts and padding_mask.  The pages' layer is trained by
+ * autograd, which keeps such activations between the passes.
+ */
+int inkling_moe_saved_size(const inkling_moe_dims_t* dims, size_t* bytes);
+
+int inkling_moe_forward_train(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                              const inkling_experts_t* experts, const uint8_t* padding_mask, void* out,
+                              void* saved, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward of InklingMoE.forward: gradients of L = sum(dout * out) for the
  * layer as inkling_moe_forward computes it (chain rule through the down
  * projection, SwiGLU, the gate_up projection and the gate's log-sigmoid
  * softmax; the correction bias only moves the top-k selection and has no
  * gradient; padded tokens skip the routed experts and keep the shared ones).
- * The routing, the gate_up activations and the permutation are recomputed
- * from x.  Every gradient buffer is overwritten, not accumulated; an expert
- * that receives no token gets zeros.
+ * The routing and the permutation are recomputed from x; the gate_up
+ * projections are read from `saved` (written by inkling_moe_forward_train
+ * with the same arguments) or, if it is NULL, recomputed, which gives the
+ * same bits.  Every gradient buffer is overwritten, not accumulated; an
+ * expert that receives no token gets zeros.
  *   dout [T][hidden] (dims->dtype);  dx [T][hidden] (dims->out_dtype), which
  *   must alias neither x nor dout.
  * Weight gradients are fp32 with the weights' layouts.
@@ -167,8 +187,9 @@ typedef struct {
 int inkling_moe_backward_workspace_size(const inkling_moe_dims_t* dims, size_t* bytes);
 
 int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
-                         const inkling_experts_t* experts, const uint8_t* padding_mask, const void* dout, void* dx,
-                         inkling_moe_grads_t* grads, void* workspace, size_t workspace_bytes, void* stream);
+                         const inkling_experts_t* experts, const uint8_t* padding_mask, const void* dout,
+                         const void* saved, void* dx, inkling_moe_grads_t* grads, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * InklingDenseMLP (layers page): the dense SwiGLU MLP on the fused interleaved

@@ -26,7 +26,8 @@ INKLING_BF16 = 1
 EXPORTED = ("inkling_moe_workspace_size", "inkling_moe_route", "inkling_moe_forward",
             "inkling_moe_strerror", "inkling_moe_last_hip_error", "inkling_moe_set_stage_events",
             "inkling_dense_mlp_workspace_size", "inkling_dense_mlp_forward",
-            "inkling_moe_backward_workspace_size", "inkling_moe_backward")
+            "inkling_moe_backward_workspace_size", "inkling_moe_backward", "inkling_moe_saved_size",
+            "inkling_moe_forward_train")
 INKLING_STAGE_EVENTS = 7
 STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "combine")
 
@@ -110,8 +111,15 @@ def load() -> ctypes.CDLL:
     lib.inkling_moe_backward_workspace_size.restype = ctypes.c_int
     lib.inkling_moe_backward.argtypes = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.POINTER(Gate),
                                          ctypes.POINTER(Experts), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                         ctypes.POINTER(Grads), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                                         ctypes.c_void_p, ctypes.POINTER(Grads), ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
     lib.inkling_moe_backward.restype = ctypes.c_int
+    lib.inkling_moe_saved_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_size_t)]
+    lib.inkling_moe_saved_size.restype = ctypes.c_int
+    lib.inkling_moe_forward_train.argtypes = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.POINTER(Gate),
+                                              ctypes.POINTER(Experts), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.inkling_moe_forward_train.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -199,9 +207,11 @@ def forward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: 
             wsh_gu: Optional[torch.Tensor], wsh_d: Optional[torch.Tensor], top_k: int, route_scale: float,
             global_scale: float, padding_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
-            out_dtype: Optional[torch.dtype] = None):
+            out_dtype: Optional[torch.dtype] = None, saved: Optional[torch.Tensor] = None):
     """inkling_moe_forward: out [T, H] (x's dtype unless out / out_dtype says
-    otherwise) and the routing dict if asked."""
+    otherwise) and the routing dict if asked.  With `saved` (uint8, saved_size
+    bytes) it is inkling_moe_forward_train, which also keeps the gate_up
+    projections there for backward()."""
     T, H = x.shape
     E, twoI, _ = w_gu.shape
     S = 0 if wsh_gu is None else wsh_gu.shape[0]
@@ -242,12 +252,32 @@ def forward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: 
     ex = Experts(w_gu.data_ptr(), w_d.data_ptr(), _ptr(wsh_gu) if S else None, _ptr(wsh_d) if S else None)
     if workspace is None:
         workspace = alloc_workspace(dims, dev)
+    if saved is not None:
+        if return_routing:
+            raise ValueError("the training forward does not return the routing")
+        if saved.dtype != torch.uint8 or not saved.is_contiguous() or saved.numel() < saved_size(dims):
+            raise ValueError("saved must be a contiguous uint8 tensor of saved_size(dims) bytes")
+        rc = load().inkling_moe_forward_train(ctypes.byref(dims), x.data_ptr(), ctypes.byref(gate), ctypes.byref(ex),
+                                              _ptr(padding_mask), out.data_ptr(), saved.data_ptr(),
+                                              workspace.data_ptr(), workspace.numel(), _stream(dev))
+        if rc != INKLING_OK:
+            raise InklingError(rc, "inkling_moe_forward_train")
+        return out
     rc = load().inkling_moe_forward(ctypes.byref(dims), x.data_ptr(), ctypes.byref(gate), ctypes.byref(ex),
                                     _ptr(padding_mask), out.data_ptr(), ro_ptr, workspace.data_ptr(),
                                     workspace.numel(), _stream(dev))
     if rc != INKLING_OK:
         raise InklingError(rc, "inkling_moe_forward")
     return (out, routing) if return_routing else out
+
+
+def saved_size(dims: Dims) -> int:
+    """inkling_moe_saved_size: bytes of the activations the training forward keeps."""
+    n = ctypes.c_size_t(0)
+    rc = load().inkling_moe_saved_size(ctypes.byref(dims), ctypes.byref(n))
+    if rc != INKLING_OK:
+        raise InklingError(rc, "inkling_moe_saved_size")
+    return n.value
 
 
 def set_stage_events(events: Optional[ctypes.Array]) -> None:
@@ -314,8 +344,10 @@ def backward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu:
              wsh_gu: Optional[torch.Tensor], wsh_d: Optional[torch.Tensor], top_k: int, route_scale: float,
              global_scale: float, dout: torch.Tensor, padding_mask: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, dx_dtype: Optional[torch.dtype] = None,
-             grads: Optional[dict] = None) -> dict:
-    """inkling_moe_backward: dict(dx, d_gate_bank, d_w_gu, d_w_d, d_wsh_gu, d_wsh_d)."""
+             grads: Optional[dict] = None, saved: Optional[torch.Tensor] = None) -> dict:
+    """inkling_moe_backward: dict(dx, d_gate_bank, d_w_gu, d_w_d, d_wsh_gu, d_wsh_d).
+    `saved`: the tensor a training forward with the same arguments filled, or
+    None to recompute the gate_up projections."""
     T, H = x.shape
     E, twoI, _ = w_gu.shape
     S = 0 if wsh_gu is None else wsh_gu.shape[0]
@@ -344,9 +376,11 @@ def backward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu:
         _need(padding_mask, "padding_mask", torch.uint8)
     if workspace is None:
         workspace = torch.empty(max(1, backward_workspace_size(dims)), dtype=torch.uint8, device=dev)
+    if saved is not None and (saved.dtype != torch.uint8 or saved.numel() < saved_size(dims)):
+        raise ValueError("saved must be the uint8 tensor of saved_size(dims) bytes a training forward filled")
     rc = load().inkling_moe_backward(ctypes.byref(dims), x.data_ptr(), ctypes.byref(gate), ctypes.byref(ex),
-                                     _ptr(padding_mask), dout.data_ptr(), grads["dx"].data_ptr(), ctypes.byref(g),
-                                     workspace.data_ptr(), workspace.numel(), _stream(dev))
+                                     _ptr(padding_mask), dout.data_ptr(), _ptr(saved), grads["dx"].data_ptr(),
+                                     ctypes.byref(g), workspace.data_ptr(), workspace.numel(), _stream(dev))
     if rc != INKLING_OK:
         raise InklingError(rc, "inkling_moe_backward")
     return grads

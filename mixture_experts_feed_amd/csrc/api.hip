@@ -257,9 +257,15 @@ int inkling_moe_route(const inkling_moe_dims_t* dims, const void* x, const inkli
     return run_route(dims, L, x, gate, padding_mask, rb, permute, workspace, (hipStream_t)stream);
 }
 
-int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
-                        const inkling_experts_t* w, const uint8_t* padding_mask, void* out,
-                        inkling_route_out_t* r, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// the forward; with `saved`, the gate_up projections are also written there
+// (fp32: routed rows [T*k][2I] in expert-sorted order, then shared [T][S*2I])
+int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                 const inkling_experts_t* w, const uint8_t* padding_mask, void* out, inkling_route_out_t* r,
+                 void* saved, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = check_dims(dims);
     if (rc != INKLING_OK) return rc;
     if (dims->T == 0) return INKLING_OK;
@@ -319,6 +325,10 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
     p.max_routed_tiles = L.max_tiles;
     p.round_counters = at<int32_t>(workspace, L.round_counters);
     p.has_routed = 1;
+    if (saved != nullptr) {
+        p.h_save_r = static_cast<float*>(saved);
+        p.h_save_sh = p.h_save_r + (size_t)dims->T * dims->top_k * 2 * dims->intermediate;
+    }
     HIP_TRY(launch_gate_up(p, s));
     HIP_TRY(mark(4, s));
     HIP_TRY(launch_down(p, s));
@@ -326,6 +336,37 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
     HIP_TRY(launch_combine(p, s));
     HIP_TRY(mark(6, s));
     return INKLING_OK;
+}
+
+size_t saved_bytes(const inkling_moe_dims_t* d) {
+    return (size_t)d->T * (size_t)(d->top_k + d->n_shared) * 2 * (size_t)d->intermediate * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                        const inkling_experts_t* w, const uint8_t* padding_mask, void* out,
+                        inkling_route_out_t* r, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_impl(dims, x, gate, w, padding_mask, out, r, nullptr, workspace, workspace_bytes, stream);
+}
+
+int inkling_moe_saved_size(const inkling_moe_dims_t* dims, size_t* bytes) {
+    const int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (bytes == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    *bytes = saved_bytes(dims);
+    return INKLING_OK;
+}
+
+int inkling_moe_forward_train(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                              const inkling_experts_t* w, const uint8_t* padding_mask, void* out, void* saved,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    const int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (dims->T > 0 && saved == nullptr) return INKLING_ERR_INVALID_ARGUMENT;
+    return forward_impl(dims, x, gate, w, padding_mask, out, nullptr, saved, workspace, workspace_bytes, stream);
 }
 
 int inkling_dense_mlp_workspace_size(const inkling_dense_dims_t* dims, size_t* bytes) {
@@ -383,8 +424,9 @@ int inkling_moe_backward_workspace_size(const inkling_moe_dims_t* dims, size_t* 
 }
 
 int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
-                         const inkling_experts_t* w, const uint8_t* padding_mask, const void* dout, void* dx,
-                         inkling_moe_grads_t* g, void* workspace, size_t workspace_bytes, void* stream) {
+                         const inkling_experts_t* w, const uint8_t* padding_mask, const void* dout,
+                         const void* saved, void* dx, inkling_moe_grads_t* g, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     int rc = check_dims(dims);
     if (rc != INKLING_OK) return rc;
     if (dims->T == 0) return INKLING_OK;
@@ -451,10 +493,20 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     p.round_counters = at<int32_t>(workspace, L.round_counters);
     p.has_routed = 1;
 
-    // 2. h = gate_up(x) per routed row and per token for the shared experts
-    void* h_r = at<void>(workspace, B.h_r);
-    void* h_sh = at<void>(workspace, B.h_sh);
-    HIP_TRY(launch_gate_up_raw(p, h_r, h_sh, s));
+    // 2. h = gate_up(x) per routed row and per token for the shared experts:
+    //    kept by inkling_moe_forward_train, else recomputed
+    const void* h_r;
+    const void* h_sh;
+    if (saved != nullptr) {
+        h_r = saved;
+        h_sh = static_cast<const float*>(saved) + (size_t)T * k * 2 * I;
+    } else {
+        void* hr = at<void>(workspace, B.h_r);
+        void* hs = at<void>(workspace, B.h_sh);
+        HIP_TRY(launch_gate_up_raw(p, hr, hs, s));
+        h_r = hr;
+        h_sh = hs;
+    }
 
     // 3. dact and the SwiGLU backward
     BwdActBufs ab = {};

@@ -92,6 +92,10 @@ struct GemmKArgs {
     void* a_shared;            // [T][S*I]
     float* dgp_routed;         // [T*k][I/64]
     float* dgp_shared;         // [T][S*I/64]
+    // kModeGateUp: optional fp32 copies of the projection (NULL: none), as
+    // h_routed / h_shared above
+    float* h_save_routed;
+    float* h_save_shared;
     // operands read as [K][N]: row strides; the shared A of kModeDAct holds the
     // S experts side by side along N (column n at element (n / a_segn_s) *
     // a_segstride_s + n % a_segn_s of a row)
@@ -926,16 +930,24 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
                             float w[4] = {v[0], v[1], v[2], v[3]};
                             store4<float>(cur.out + (size_t)(cur.t0 + m) * cur.N + n, w);
                         } else if (MODE == kModeGateUp) {
+                            // optional fp32 copy of the projection itself (kept for the backward)
+                            float* hs = cur.is_shared ? a.h_save_shared : a.h_save_routed;
                             if (cur.is_shared) {
                                 const int t = cur.t0 + m;
                                 const float g = (n / (2 * a.I) == ep_s0) ? ep_g0[j] : ep_g1[j];
                                 TE* o = reinterpret_cast<TE*>(a.out_shared) + (size_t)t * a.S * a.I + (n >> 1);
                                 store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
+                                if (hs != nullptr) hs += (size_t)t * cur.N + n;
                             } else {
                                 const int row = cur.grow0 + m;
                                 const float g = ep_g0[j];
                                 TE* o = reinterpret_cast<TE*>(a.out_routed) + (size_t)row * a.I + (n >> 1);
                                 store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
+                                if (hs != nullptr) hs += (size_t)row * cur.N + n;
+                            }
+                            if (hs != nullptr) {
+                                float w[4] = {v[0], v[1], v[2], v[3]};
+                                store4<float>(hs, w);
                             }
                         } else {
                             // fp32 rows: the layer output is rounded once, in the combine
@@ -1078,6 +1090,8 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     a.A_routed = p.w_gu;
     a.B_routed = p.x;
     a.out_routed = p.act_r;
+    a.h_save_routed = p.h_save_r;
+    a.h_save_shared = p.h_save_sh;
     a.K_r = p.H;
     a.N_r = 2 * p.I;
     a.ntn_r = (a.N_r + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);

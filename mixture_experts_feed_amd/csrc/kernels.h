@@ -60,6 +60,8 @@ struct MoeGemmParams {
     void* y;       // [T*k][H] fp32, slot rows
     void* ysh;     // [T][H] fp32
     void* out;     // [T][H]
+    float* h_save_r;   // optional: gate_up projection of the routed rows [T*k][2I] fp32 (sorted rows)
+    float* h_save_sh;  // optional: ... of the shared experts [T][S*2I] fp32
     int32_t* round_counters;   // kRoundCounters ints, zero before gate_up
     int has_routed;            // 0: shared tiles only (dense MLP); tiles / num_tiles unused
     int max_routed_tiles;

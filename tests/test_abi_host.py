@@ -187,14 +187,40 @@ def test_backward_argument_checks(lib):
     gr = B.Grads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
     x, dout, dx, ws = (ctypes.c_void_p(v) for v in (0x4000, 0x5000, 0x6000, 0x7000))
     bw = lib.inkling_moe_backward
-    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, None, dx, ctypes.byref(gr), ws,
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, None, None, dx, ctypes.byref(gr), ws,
               n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
-    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, dout, ctypes.byref(gr), ws,
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, None, dout, ctypes.byref(gr), ws,
               n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
     no_sh = B.Grads(0x1000, 0x1000, 0x1000, None, None)
-    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, dx, ctypes.byref(no_sh), ws,
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, None, dx, ctypes.byref(no_sh), ws,
               n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
-    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, dx, ctypes.byref(gr), ws,
+    assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, None, dx, ctypes.byref(gr), ws,
               n.value - 1, None) == B.INKLING_ERR_WORKSPACE
     bad = _dims(hidden=96)
     assert lib.inkling_moe_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == B.INKLING_ERR_UNSUPPORTED
+
+
+def test_training_forward_argument_checks(lib):
+    """saved_size = (T*top_k + T*n_shared) * 2I fp32; the training forward needs
+    its saved buffer and checks its other arguments as the forward does."""
+    d = _dims()
+    n = ctypes.c_size_t(0)
+    assert lib.inkling_moe_saved_size(ctypes.byref(d), ctypes.byref(n)) == B.INKLING_OK
+    assert n.value == d.T * (d.top_k + d.n_shared) * 2 * d.intermediate * 4
+    assert lib.inkling_moe_saved_size(ctypes.byref(d), None) == B.INKLING_ERR_INVALID_ARGUMENT
+    bad = _dims(hidden=96)
+    assert lib.inkling_moe_saved_size(ctypes.byref(bad), ctypes.byref(n)) == B.INKLING_ERR_UNSUPPORTED
+    nw = ctypes.c_size_t(0)
+    lib.inkling_moe_workspace_size(ctypes.byref(d), ctypes.byref(nw))
+    gate = B.Gate(0x1000, 0x1000, 1.0, 1.0)
+    ex = B.Experts(0x1000, 0x1000, 0x1000, 0x1000)
+    x, out, saved, ws = (ctypes.c_void_p(v) for v in (0x4000, 0x5000, 0x6000, 0x7000))
+    ft = lib.inkling_moe_forward_train
+    assert ft(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, out, None, ws, nw.value,
+              None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert ft(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, x, saved, ws, nw.value,
+              None) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert ft(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, out, saved, ws, nw.value - 1,
+              None) == B.INKLING_ERR_WORKSPACE
+    zero = _dims(T=0)
+    assert ft(ctypes.byref(zero), None, None, None, None, None, None, None, 0, None) == B.INKLING_OK
