@@ -305,12 +305,14 @@ def main():
     if not args.no_others and w.name == "prefill_h6144":
         # the other two TFLOP/s workloads: skewed routing (same weights) and the small bf16 shape
         result["other_workloads"] = {}
-        for oname in ("skewed_h6144", "small_bf16"):
+        for oname in ("skewed_h6144", "small_bf16", "ep8_shard_h6144"):
             ow = wl.WORKLOADS[oname]
-            oinp = wl.make_inputs(ow, device=dev, with_experts=ow.hidden != w.hidden)
-            if ow.hidden == w.hidden:
-                for k in ("w_gu", "w_d", "wsh_gu", "wsh_d"):
-                    oinp[k] = inp[k]
+            same_shape = ow.hidden == w.hidden and ow.intermediate == w.intermediate and ow.n_shared == S
+            oinp = wl.make_inputs(ow, device=dev, with_experts=not same_shape)
+            if same_shape:
+                # the prefill weights (the first n_routed routed experts)
+                oinp["w_gu"], oinp["w_d"] = inp["w_gu"][:ow.n_routed], inp["w_d"][:ow.n_routed]
+                oinp["wsh_gu"], oinp["wsh_d"] = inp["wsh_gu"], inp["wsh_d"]
             odims = B.make_dims(ow.T, ow.hidden, ow.n_routed, ow.top_k, ow.n_shared, ow.intermediate, ow.torch_dtype)
             ows = B.alloc_workspace(odims, dev)
             oout = torch.empty_like(oinp["x"])

@@ -108,6 +108,15 @@ WORKLOADS: Dict[str, Workload] = {
         "inkling_default_h6144", T=8192, hidden=6144, n_routed=256, top_k=6, n_shared=2, intermediate=3072,
         dtype="bf16", route_scale=8.0, global_scale=1.0,
         gate_dist=("uniform", 0.05), bias_dist=("uniform", 0.05), family_seed=0, x_seed=0),
+    # the GEMM shapes of one GPU's share of the prefill layer under 8-way
+    # expert parallelism: 1024 local tokens through the replicated shared
+    # experts, and 16 local experts receiving T*k/8 = 8192 routed rows (about
+    # 512 each); the routing here is local, where a real dispatch would bring
+    # the rows from every GPU
+    "ep8_shard_h6144": Workload(
+        "ep8_shard_h6144", T=1024, hidden=6144, n_routed=16, top_k=8, n_shared=2, intermediate=2048,
+        dtype="bf16", route_scale=2.5, global_scale=1.0,
+        gate_dist=("uniform", 0.05), bias_dist=("uniform", 0.05), family_seed=0, x_seed=0),
     "skewed_h6144": Workload(
         "skewed_h6144", T=16384, hidden=6144, n_routed=128, top_k=8, n_shared=2, intermediate=2048,
         dtype="bf16", route_scale=2.5, global_scale=1.0,

@@ -214,6 +214,18 @@ def test_skewed_h6144(h6144_experts):
     _sampled_parity("skewed_h6144", h6144_experts)
 
 
+def test_ep8_shard_h6144():
+    """One GPU's share of the prefill layer under 8-way expert parallelism
+    (16 local experts, about 512 rows each, 1024 local tokens) at full width."""
+    w = wl.WORKLOADS["ep8_shard_h6144"]
+    experts = wl.expert_weights(w, device=DEV)
+    try:
+        _sampled_parity("ep8_shard_h6144", experts, n_sample=24)
+    finally:
+        del experts
+        torch.cuda.empty_cache()
+
+
 def test_inkling_default_h6144():
     """Inkling's own MoE shape (configuration page defaults: 256 routed experts,
     top-6, 2 shared, intermediate 3072, route_scale 8) at full width."""
