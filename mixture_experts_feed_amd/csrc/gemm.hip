@@ -130,7 +130,10 @@ __device__ __forceinline__ void mma16<float>(f32x4_t& acc, const uint4& a, const
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// sigmoid through the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an
+// IEEE division sequence; exp overflow gives 1/inf = 0, the right limit
+__device__ __forceinline__ float sigmoid(float v) { return __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
+__device__ __forceinline__ float silu(float v) { return v * sigmoid(v); }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const float gg = hv[2 * r], uu = hv[2 * r + 1];
-                                const float sg = 1.0f / (1.0f + __expf(-gg));
+                                const float sg = sigmoid(gg);
                                 const float si = gg * sg;
                                 const float pp = si * uu;
                                 const float da = acc[i][j][r];
