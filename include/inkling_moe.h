@@ -45,7 +45,7 @@
  *
  * Limits (INKLING_ERR_UNSUPPORTED otherwise): hidden % 64 == 0,
  * intermediate % 64 == 0, 1 <= top_k <= min(n_routed, 32), n_routed <= 512,
- * n_routed + n_shared <= 512, n_shared <= 16, T * top_k < 2^31.
+ * n_routed + n_shared <= 512, n_shared <= 16, T * top_k <= 2^31 - 257.
  */
 #ifndef INKLING_MOE_H
 #define INKLING_MOE_H

@@ -38,8 +38,8 @@ int check_dims(const inkling_moe_dims_t* d) {
     if (d->hidden % 64 != 0 || d->intermediate % 64 != 0) return INKLING_ERR_UNSUPPORTED;
     if (d->n_routed > 512 || d->n_routed + d->n_shared > 512 || d->top_k > 32 || d->n_shared > 16)
         return INKLING_ERR_UNSUPPORTED;
-    // int32 row / slot indices
-    if (d->T * (int64_t)d->top_k > INT32_MAX) return INKLING_ERR_UNSUPPORTED;
+    // int32 row / slot indices (and token counts padded to 256)
+    if (d->T * (int64_t)d->top_k > INT32_MAX - 256) return INKLING_ERR_UNSUPPORTED;
     return INKLING_OK;
 }
 

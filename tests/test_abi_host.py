@@ -77,6 +77,7 @@ def test_workspace_size_grows_with_tokens(lib):
     (dict(n_routed=600, top_k=2), B.INKLING_ERR_UNSUPPORTED),
     (dict(n_routed=64, top_k=33), B.INKLING_ERR_UNSUPPORTED),
     (dict(n_shared=17), B.INKLING_ERR_UNSUPPORTED),
+    (dict(T=2 ** 30, top_k=2), B.INKLING_ERR_UNSUPPORTED),   # T * top_k past the int32 slot indices
 ])
 def test_invalid_dims_rejected(lib, kw, code):
     rc, _ = _ws(lib, **kw)
@@ -224,3 +225,12 @@ def test_training_forward_argument_checks(lib):
               None) == B.INKLING_ERR_WORKSPACE
     zero = _dims(T=0)
     assert ft(ctypes.byref(zero), None, None, None, None, None, None, None, 0, None) == B.INKLING_OK
+
+
+def test_largest_token_count_accepted(lib):
+    """T * top_k = 2^31 - 257 is the largest accepted slot count (only the size
+    query runs; nothing is allocated)."""
+    rc, n = _ws(lib, T=2 ** 31 - 257, top_k=1)
+    assert rc == B.INKLING_OK and n > 0
+    rc, _ = _ws(lib, T=2 ** 31 - 256, top_k=1)
+    assert rc == B.INKLING_ERR_UNSUPPORTED
