@@ -276,9 +276,7 @@ hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, 
                              const int32_t* topk_idx, const float* dzc, const float* bank, void* dx, int T, int H,
                              int E, int S, int k, hipStream_t stream) {
     const size_t items = (size_t)T * (H / 4);
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int blocks = (int)std::min<size_t>((items + 255) / 256, (size_t)std::max(cus, 1) * 16);
+    const int blocks = (int)std::min<size_t>((items + 255) / 256, (size_t)device_cu_count() * 16);
     if (out_dtype == 1)
         hipLaunchKernelGGL(dx_combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, dxr, dxs, pos, topk_idx, dzc,
                            bank, (bf16_t*)dx, T, H, E, S, k);

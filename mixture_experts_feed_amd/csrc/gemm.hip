@@ -1026,18 +1026,7 @@ constexpr int kPrefillBN = 256;
 constexpr int kDecodeBN = 128, kDecodeStages = 4, kDecodeRowB = 128, kDecodeGridPerCU = 1;
 int cfg_bn(int cfg) { return cfg == 0 ? kPrefillBN : kDecodeBN; }
 
-int num_cus() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
+int num_cus() { return device_cu_count(); }
 
 template <typename TE, int MODE>
 hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t stream) {
@@ -1086,6 +1075,19 @@ GemmKArgs base_args(const MoeGemmParams& p) {
 }
 
 }  // namespace
+
+int device_cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
 
 int gemm_cfg_for(int T, int E, int k) {
     const double rows_per_expert = (double)T * k / E;

@@ -36,6 +36,10 @@ hipError_t launch_permute_small(const int32_t* topk_idx, const float* topk_w, co
                                 int32_t* round_counters, int32_t* sorted_slots, int32_t* row_token, float* row_gamma,
                                 int32_t* pos, hipStream_t stream);
 
+// compute units of the current device, queried once per process (256 if the
+// query fails)
+int device_cu_count();
+
 // ---- grouped GEMMs and combine (gemm.hip) ---------------------------------
 struct MoeGemmParams {
     int dtype;       // 0 f32, 1 bf16: x, weights, act
