@@ -568,6 +568,7 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     wd.K_s = B.Tpad;
     wd.out_r = g->d_routed_down;
     wd.out_s = g->d_shared_down;
+    wd.counters = p.round_counters + 24;
     HIP_TRY(launch_wgrad(wd, s));
     WgradParams wg = wd;   // d gate_up[e][n][h] = sum_r dh[r][n] x[t(r)][h]
     wg.M = 2 * I;
@@ -584,6 +585,7 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     wg.b_sh_stride = (long long)2 * I;
     wg.out_r = g->d_routed_gate_up;
     wg.out_s = g->d_shared_gate_up;
+    wg.counters = p.round_counters + 32;
     HIP_TRY(launch_wgrad(wg, s));
     return INKLING_OK;
 }

@@ -41,9 +41,12 @@ constexpr int kWave = 64;
 
 // Tile descriptor of the routed grouped GEMMs: expert id and first row of the
 // tile within that expert's block of expert-sorted rows.
-// Per-XCD tile-round counters of the grouped GEMM launches (8 each: gate_up,
-// down, and the backward's dact).
-constexpr int kRoundCounters = 24;
+// Per-XCD counters of the grouped GEMM launches (8 each: gate_up or the
+// backward's recompute of it, down or dx, dact, and the two weight-gradient
+// launches): tiles finished (tile-round rendezvous) or tiles taken (tile
+// queue).  Written to zero by the permutation (the dense MLP: its prep
+// kernel) before each use.
+constexpr int kRoundCounters = 40;
 
 struct RoutedTile {
     int32_t expert;

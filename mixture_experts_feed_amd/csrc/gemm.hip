@@ -52,6 +52,13 @@ template <int MODE>
 constexpr bool a_kn() { return MODE == kModeDAct || MODE == kModeDx || MODE == kModeWgrad; }
 template <int MODE>
 constexpr bool b_kn() { return MODE == kModeWgrad; }
+// How the workgroups of an XCD walk its range of tiles after their first:
+// kSchedStride: with stride = workgroups per XCD;
+// kSchedRound: the same, meeting at the end of every round of tiles (below);
+// kSchedQueue: each takes the next tile of the range from the XCD's counter,
+//              so the tiles in flight on an XCD stay a contiguous window of
+//              the range.
+enum { kSchedStride = 0, kSchedRound = 1, kSchedQueue = 2 };
 constexpr int kSpinLimit = 400;   // polls of a tile-round wait (about 100-400 us at most)
 constexpr int kWgradEpi = 256;    // K-equivalent cost of a weight-gradient tile's fp32 epilogue
 // Cache policy of the weight (A) loads.  Tiles of at most 16 token rows (the
@@ -84,7 +91,7 @@ struct GemmKArgs {
     int seg_s;              // shared A(n, kk) = A_shared + (kk/seg)*N_s*seg + n*seg + kk%seg
     int shared_blocks, shared_mtiles;
     int has_routed;
-    int32_t* round_counter;    // [8]: tiles finished per XCD (zero at launch)
+    int32_t* round_counter;    // [8] per XCD, zero at launch: tiles finished (kSchedRound) or taken (kSchedQueue)
     // kModeDAct
     const void* h_routed;      // [T*k][2I] sorted rows, fp32
     const void* h_shared;      // [T][S*2I] fp32
@@ -350,7 +357,7 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
 // Persistent grouped GEMM.  A workgroup owns a contiguous range of grouped
 // tiles on its XCD (blocks are dealt to the 8 XCDs round-robin, so workgroups
 // that run side by side on one XCD share that range's operands through its L2)
-// and walks the range with stride = workgroups per XCD.  BN weight rows x BM
+// and walks the range as SCHED says (kSchedStride, kSchedRound, kSchedQueue).  BN weight rows x BM
 // token rows per tile; WN x WM waves (8, two per SIMD); SA weight and SB token
 // LDS pipeline stages of ROWB bytes of K per row, filled by direct global->LDS
 // loads.  TE: operand and intermediate type.
@@ -362,7 +369,7 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
 // stage that is already complete.  The first stages of the next tile are
 // loaded before the epilogue of the current one, so the epilogue's stores and
 // SwiGLU arithmetic overlap the next tile's load latency.
-template <typename TE, int BN, int BM, int WN, int WM, int SA, int SB, int ROWB, int GM, int SYNC, int MODE>
+template <typename TE, int BN, int BM, int WN, int WM, int SA, int SB, int ROWB, int GM, int SCHED, int MODE>
 __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs a) {
     constexpr int NW = WN * WM;                     // waves per workgroup
     static_assert(NW == 8, "eight waves: two per SIMD");
@@ -484,6 +491,16 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     const int L_end = range_start(xcd + 1);
     int L = L_beg + (blockIdx.x >> 3);
     if (L >= L_end) return;
+    // kSchedQueue: tiles L_beg + nloc + q for q = 0, 1, ... of the XCD's counter
+    // (zero at launch); thread 0 draws the next one while the current tile
+    // runs and hands it to the workgroup through LDS
+    __shared__ int q_next;
+    int q_val = 0;
+    auto draw = [&]() __attribute__((always_inline)) {
+        if constexpr (SCHED == kSchedQueue)
+            if (tid == 0)
+                q_val = __hip_atomic_fetch_add(a.round_counter + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
 
     // ---- load sources and the stage issue -------------------------------------
     // LDS rows are ROWB bytes; the 16-byte chunk c of row r sits at chunk
@@ -712,7 +729,7 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         else return read_kn32(st, ks, 16 * (WM * j + wm), RBB);
     };
 
-    // Tile-round rendezvous of an XCD (SYNC): every workgroup counts each tile
+    // Tile-round rendezvous of an XCD (kSchedRound): every workgroup counts each tile
     // it finishes on its XCD's counter and waits, for at most kSpinLimit polls,
     // until every workgroup of its round has finished, so that the workgroups
     // that share tiles through L2 start the next round together.  (Meeting
@@ -822,10 +839,11 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     setup(cur);
     issue_first(cur.K / BK);
     prefetch_epilogue(cur);
+    draw();
 
     while (true) {
         const int nk = cur.K / BK;
-        if constexpr (SYNC) sync_round = (L - L_beg) / nloc;
+        if constexpr (SCHED == kSchedRound) sync_round = (L - L_beg) / nloc;
         // token blocks / weight-row blocks of this wave that hold valid rows
         const int nvb_all = (cur.rows_valid + 15) >> 4;
         const int nvb = min(FM, max(0, (nvb_all - wm + WM - 1) / WM));
@@ -844,20 +862,30 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
         }
 
         // all waves are done reading the stages: start loading the next tile
-        L += nloc;
+        if constexpr (SCHED == kSchedQueue) {
+            // (no loads are in flight here: the last stage waited for all)
+            if (tid == 0) q_next = q_val;
+            __syncthreads();
+            L = L_beg + nloc + q_next;
+        } else {
+            L += nloc;
+        }
         const bool has_next = L < L_end;
-        if constexpr (SYNC) {
+        if constexpr (SCHED == kSchedRound) {
             // end of the tile: round r + 1 starts once round r is done by all
             // (with a next tile, rounds 0..r are full)
             rendezvous((long long)nloc * (sync_round + 1), has_next);
         }
-        wait_lgkmcnt0();
-        barrier_keep_loads();
+        if constexpr (SCHED != kSchedQueue) {
+            wait_lgkmcnt0();
+            barrier_keep_loads();
+        }
         Tile<TE> nxt = cur;
         if (has_next) {
             nxt = decode_tile<TE, BM, GM, MODE>(a, L, BN);
             setup(nxt);
             issue_first(nxt.K / BK);
+            draw();
         }
 
         // ---- epilogue of the current tile ----------------------------------
@@ -1017,10 +1045,16 @@ __global__ __launch_bounds__(256) void dense_prep_kernel(float* __restrict__ gam
 // cfg 1 (few rows per expert, decode): 128 weight rows x 16 tokens, 8 waves
 //       along the weight rows, 4 stages.
 constexpr int kPrefillStagesA = 2, kPrefillStagesB = 2, kPrefillRowB = 128;
-// tile-round rendezvous per XCD: pays off for the long-K gate_up tiles only,
-// and only with at least kSyncMinRounds rounds of tiles (measured: 4.6% faster
-// gate_up at 28 rounds, 10% slower at 4)
-constexpr int kPrefillSyncGateUp = 1, kPrefillSyncDown = 0;
+// Tile order on an XCD (measured at T=8192, hidden 6144):
+// - long-K tiles (gate_up and its backward twins, K = hidden): the tile-round
+//   rendezvous, with at least kSyncMinRounds rounds of tiles (4.6% faster
+//   gate_up at 28 rounds, 10% slower at 4); the queue was 4% slower there;
+// - short-K tiles (down, dx, weight gradients): the queue (down 1-3%, the
+//   backward 3% faster than the plain stride; the rendezvous was slower).
+template <int MODE>
+constexpr int prefill_sched() {
+    return MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kSchedRound : kSchedQueue;
+}
 constexpr int kSyncMinRounds = 8;
 constexpr int kPrefillBN = 256;
 constexpr int kDecodeBN = 128, kDecodeStages = 4, kDecodeRowB = 128, kDecodeGridPerCU = 1;
@@ -1034,18 +1068,18 @@ hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t s
     // persistent: at most one workgroup per CU (LDS), a multiple of the 8 XCDs
     int grid = std::min(max_tiles, num_cus() * (cfg == 0 ? 1 : kDecodeGridPerCU));
     grid = (grid + 7) / 8 * 8;
-    constexpr int kSync = MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kPrefillSyncGateUp
-                          : MODE == kModeDown ? kPrefillSyncDown : 0;
+    constexpr int kSched = prefill_sched<MODE>();
     // the backward modes run the 256 x 256 tiles only
     if (cfg == 0 || MODE == kModeWgrad || a_kn<MODE>()) {
-        if (kSync && max_tiles >= kSyncMinRounds * num_cus())
+        if (kSched == kSchedQueue || (kSched == kSchedRound && max_tiles >= kSyncMinRounds * num_cus()))
             hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB,
-                                               kPrefillRowB, 4, kSync, MODE>), dim3(grid), dim3(512), 0, stream, a);
+                                               kPrefillRowB, 4, kSched, MODE>), dim3(grid), dim3(512), 0, stream, a);
         else
             hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB,
-                                               kPrefillRowB, 4, 0, MODE>), dim3(grid), dim3(512), 0, stream, a);
+                                               kPrefillRowB, 4, kSchedStride, MODE>), dim3(grid), dim3(512), 0,
+                               stream, a);
     } else if constexpr (!a_kn<MODE>())
-        hipLaunchKernelGGL((moe_gemm_kernel<TE, kDecodeBN, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, 0, MODE>), dim3(grid),
+        hipLaunchKernelGGL((moe_gemm_kernel<TE, kDecodeBN, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, kSchedStride, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
     return hipGetLastError();
 }
@@ -1282,6 +1316,7 @@ hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream) {
     a.wg_mtiles = (w.M + 255) / 256;
     a.wg_ntiles = (w.N + kPrefillBN - 1) / kPrefillBN;
     a.w_out_routed = w.out_r;
+    a.round_counter = w.counters;
     a.w_out_shared = w.out_s;
     const int tiles = (w.E + w.S) * a.wg_mtiles * a.wg_ntiles;
     if (w.dtype == 1) return launch_mode<bf16_t, kModeWgrad>(0, a, tiles, stream);

@@ -119,6 +119,7 @@ struct WgradParams {
     long long a_sh_stride, b_sh_stride;
     float* out_r;
     float* out_s;
+    int32_t* counters;   // 8 ints, zero at launch (the tile queue of each XCD)
 };
 hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream);
 
