@@ -419,6 +419,10 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
     __shared__ __attribute__((aligned(16))) uint8_t sb5[SB > 5 ? B_BYTES : SMALL];
     __shared__ __attribute__((aligned(16))) uint8_t sb6[SB > 6 ? B_BYTES : SMALL];
     __shared__ __attribute__((aligned(16))) uint8_t sb7[SB > 7 ? B_BYTES : SMALL];
+    // epilogue staging (256 x 256 tiles): per wave 16 rows of kEpRowB bytes
+    constexpr int kEpRowB = 144;   // 128 bytes of a row + 16 of padding
+    constexpr bool kEpLds = FN == 4 && MODE != kModeDAct;
+    __shared__ __attribute__((aligned(16))) uint8_t ep_lds[kEpLds ? NW * 16 * kEpRowB : SMALL];
     auto stage_a = [&](auto S_) -> uint8_t* {
         constexpr int i = decltype(S_)::value % SA;
         if constexpr (i == 0) return sa0;
@@ -942,9 +946,94 @@ __global__ __launch_bounds__(WN * WM * 64) void moe_gemm_kernel(const GemmKArgs 
                 }
             }
         }
+        if constexpr (kEpLds) {
+            // The wave's results go through its LDS block, 16 rows at a time,
+            // so that a global store writes whole row segments (4 or 8 rows of
+            // 128 bytes, or 16 rows of 64) instead of 16 rows of 4-16 bytes:
+            // phase A writes the lane's values in the MFMA layout, phase B
+            // reads 16-byte chunks of rows and stores them.  LDS operations of
+            // one wave complete in order, so no barrier is needed.
+            // (lane-derived offsets are recomputed for every tile: hoisted out
+            // of the tile loop, the compiler would keep dozens of them live
+            // across the K loop and spill them)
+            int ln = lane;
+            __asm__ volatile("" : "+v"(ln));
+            const int g4 = ln >> 4, rw = ln & 15;
+            uint8_t* __restrict__ ep = ep_lds + wv * 16 * kEpRowB;
+            // fp32 columns wn0 .. wn0 + 63 of the 16 rows from mb, in two
+            // halves of 32 columns; rowp(r): output row of row mb + r at
+            // column n0 + wn0 (nullptr: none)
+            auto flush_f32 = [&](int j, int mb, auto rowp) __attribute__((always_inline)) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                    for (int i = 2 * hh; i < 2 * hh + 2; ++i)
+                        if (i < nvi)
+                            *reinterpret_cast<f32x4_t*>(ep + rw * kEpRowB + ((i - 2 * hh) * 16 + 4 * g4) * 4) = acc[i][j];
+#pragma unroll
+                    for (int sgi = 0; sgi < 2; ++sgi) {
+                        const int c = ln + 64 * sgi, r = c >> 3, q = c & 7;
+                        const f32x4_t d = *reinterpret_cast<const f32x4_t*>(ep + r * kEpRowB + q * 16);
+                        float* o = rowp(r);
+                        if (o != nullptr && mb + r < cur.rows_valid && 2 * hh + (q >> 2) < nvi)
+                            *reinterpret_cast<f32x4_t*>(o + 32 * hh + 4 * q) = d;
+                    }
+                }
+            };
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                if (j >= nvb) continue;
+                const int mb = 16 * (WM * j + wm);
+                if constexpr (MODE == kModeGateUp) {
+                    // act = gamma silu(g) u of the interleaved pairs: the wave's
+                    // 64 projection columns give 32 act columns per row
+                    const float g0 = ep_g0[j], g1 = ep_g1[j];
+#pragma unroll
+                    for (int i = 0; i < FN; ++i) {
+                        if (i < nvi) {
+                            const f32x4_t v = acc[i][j];
+                            const int n = cur.n0 + wn0 + 16 * i + 4 * g4;
+                            const float g = cur.is_shared && n / (2 * a.I) != ep_s0 ? g1 : g0;
+                            store2<TE>(reinterpret_cast<TE*>(ep + rw * kEpRowB + (8 * i + 2 * g4) * sizeof(TE)),
+                                       silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
+                        }
+                    }
+                    constexpr int CPR = 32 * (int)sizeof(TE) / 16;   // 16-byte chunks per row
+                    const int ld = cur.is_shared ? a.S * a.I : a.I;
+                    TE* obase = reinterpret_cast<TE*>(cur.is_shared ? a.out_shared : a.out_routed) +
+                                (size_t)(cur.is_shared ? cur.t0 : cur.grow0) * ld + ((cur.n0 + wn0) >> 1);
+#pragma unroll
+                    for (int sgi = 0; sgi < 16 * CPR / 64; ++sgi) {
+                        const int c = ln + 64 * sgi, r = c / CPR, q = c % CPR;
+                        const uint4 d = *reinterpret_cast<const uint4*>(ep + r * kEpRowB + q * 16);
+                        const int col = q * (16 / (int)sizeof(TE));
+                        if (mb + r < cur.rows_valid && col / 8 < nvi)
+                            *reinterpret_cast<uint4*>(obase + (size_t)(mb + r) * ld + col) = d;
+                    }
+                    // optional fp32 copy of the projection itself (kept for the backward)
+                    float* hs = cur.is_shared ? a.h_save_shared : a.h_save_routed;
+                    if (hs != nullptr) {
+                        float* hb = hs + (size_t)(cur.is_shared ? cur.t0 : cur.grow0) * cur.N + cur.n0 + wn0;
+                        flush_f32(j, mb, [&](int r) -> float* { return hb + (size_t)(mb + r) * cur.N; });
+                    }
+                } else if constexpr (MODE == kModeGateUpRaw) {   // h kept in fp32 (not an MFMA operand)
+                    float* hb = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) +
+                                (size_t)(cur.is_shared ? cur.t0 : cur.grow0) * cur.N + cur.n0 + wn0;
+                    flush_f32(j, mb, [&](int r) -> float* { return hb + (size_t)(mb + r) * cur.N; });
+                } else if constexpr (MODE == kModeWgrad) {
+                    float* hb = cur.out + (size_t)cur.t0 * cur.N + cur.n0 + wn0;
+                    flush_f32(j, mb, [&](int r) -> float* { return hb + (size_t)(mb + r) * cur.N; });
+                } else {
+                    // fp32 rows: the layer output is rounded once, in the combine
+                    float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) + cur.n0 + wn0;
+                    const int er = ep_row[j];
+                    flush_f32(j, mb, [&](int r) -> float* { return o + (size_t)__shfl(er, r) * a.H; });
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
-            if constexpr (MODE == kModeDAct) break;
+            if constexpr (MODE == kModeDAct || kEpLds) break;
             const int m = 16 * (WM * j + wm) + rl;
             if (j < nvb && m < cur.rows_valid) {
 #pragma unroll
