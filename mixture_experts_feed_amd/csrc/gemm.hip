@@ -58,7 +58,12 @@ constexpr bool b_kn() { return MODE == kModeWgrad; }
 // kSchedQueue: each takes the next tile of the range from the XCD's counter,
 //              so the tiles in flight on an XCD stay a contiguous window of
 //              the range.
-enum { kSchedStride = 0, kSchedRound = 1, kSchedQueue = 2 };
+// kSchedGroup: each takes the next tile from the counter once it is free, then
+//              waits (at most kSpinLimit polls) until every tile of its partner
+//              group (the row tiles that read its weight tile, at most
+//              kGroupMax of them) has been taken, so that they start together.
+enum { kSchedStride = 0, kSchedRound = 1, kSchedQueue = 2, kSchedGroup = 3 };
+constexpr int kGroupMax = 8;
 constexpr int kSpinLimit = 400;   // polls of a tile-round wait (about 100-400 us at most)
 constexpr int kWgradEpi = 128;    // K-equivalent cost of a weight-gradient tile's fp32 epilogue
 // Cache policy of the weight (A) loads.  Tiles of at most 16 token rows (the
@@ -259,11 +264,13 @@ struct Tile {
     const TE* A;
     const TE* B;
     float* out;          // kModeWgrad: this problem's gradient [M][N]
+    int gend;            // end of the tile's partner group (tiles gend - n .. gend - 1)
 };
 
 template <typename TE, int BM, int GM, int MODE>
 __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int BN) {
     Tile<TE> t;
+    t.gend = L + 1;
     t.grow0 = 0;
     t.t0 = 0;
     t.out = nullptr;
@@ -306,6 +313,11 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
     if (t.is_shared) {
         int mt, nt;
         grouped<GM>(L, a.shared_mtiles, a.ntn_s, mt, nt);
+        {
+            // partners: the row tiles of this column tile in its group of GM
+            const int first = (mt / GM) * GM, gm = min(GM, a.shared_mtiles - first);
+            t.gend = L - (mt - first) + min(gm, kGroupMax);
+        }
         t.t0 = mt * BM;
         t.rows_valid = min(BM, a.T - t.t0);
         t.n0 = nt * BN;
@@ -334,6 +346,12 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
         const int l = l0 - tb * a.ntn_r;
         const int nt = l / c;
         const int row_start = (l - nt * c) * BM;
+        {
+            // partners: the expert's row tiles for weight tile nt, in runs of
+            // at most kGroupMax
+            const int j = l - nt * c, run0 = L - j + kGroupMax * (j / kGroupMax);
+            t.gend = min(L - j + c, run0 + kGroupMax);
+        }
         const RoutedTile tl = {tl0.expert, row_start};
         t.rows_valid = min(BM, cnt - row_start);
         t.grow0 = base + row_start;
@@ -357,7 +375,8 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
 // Persistent grouped GEMM.  A workgroup owns a contiguous range of grouped
 // tiles on its XCD (blocks are dealt to the 8 XCDs round-robin, so workgroups
 // that run side by side on one XCD share that range's operands through its L2)
-// and walks the range as SCHED says (kSchedStride, kSchedRound, kSchedQueue).  BN weight rows x BM
+// and walks the range as SCHED says (kSchedStride, kSchedRound, kSchedQueue,
+// kSchedGroup).  BN weight rows x BM
 // token rows per tile; WN x WM waves (8, two per SIMD; or 4 with two workgroups
 // per CU); SA weight and SB token
 // LDS pipeline stages of ROWB bytes of K per row, filled by direct global->LDS
@@ -505,6 +524,20 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
         if constexpr (SCHED == kSchedQueue)
             if (tid == 0)
                 q_val = __hip_atomic_fetch_add(a.round_counter + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // kSchedGroup: before a tile's K loop, thread 0 waits until the counter
+    // has handed out every partner tile of its range (the K loop's first
+    // barrier holds the other threads)
+    auto group_wait = [&](const Tile<TE>& t) __attribute__((always_inline)) {
+        if constexpr (SCHED == kSchedGroup) {
+            const int need = min(t.gend, L_end) - (L_beg + nloc);   // counter value that covers the group
+            if (tid == 0 && need > 0)
+                for (int it = 0; it < kSpinLimit; ++it) {
+                    if (__hip_atomic_load(a.round_counter + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need)
+                        break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+        }
     };
 
     // ---- load sources and the stage issue -------------------------------------
@@ -867,7 +900,13 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
         }
 
         // all waves are done reading the stages: start loading the next tile
-        if constexpr (SCHED == kSchedQueue) {
+        if constexpr (SCHED == kSchedGroup) {
+            // the next tile is taken now that this workgroup is free
+            if (tid == 0)
+                q_next = __hip_atomic_fetch_add(a.round_counter + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            L = L_beg + nloc + q_next;
+        } else if constexpr (SCHED == kSchedQueue) {
             // (no loads are in flight here: the last stage waited for all)
             if (tid == 0) q_next = q_val;
             __syncthreads();
@@ -881,7 +920,7 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
             // (with a next tile, rounds 0..r are full)
             rendezvous((long long)nloc * (sync_round + 1), has_next);
         }
-        if constexpr (SCHED != kSchedQueue) {
+        if constexpr (SCHED != kSchedQueue && SCHED != kSchedGroup) {
             wait_lgkmcnt0();
             barrier_keep_loads();
         }
@@ -1087,6 +1126,7 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
         if (!has_next) break;
         cur = nxt;
         prefetch_epilogue(cur);
+        group_wait(cur);
     }
 }
 
@@ -1143,7 +1183,10 @@ constexpr int kPrefillGM = 8;
 // Tile order on an XCD (measured at T=8192, hidden 6144):
 // - long-K tiles (gate_up and its backward twins, K = hidden): the tile-round
 //   rendezvous, with at least kSyncMinRounds rounds of tiles (4.6% faster
-//   gate_up at 28 rounds, 10% slower at 4); the queue was 4% slower there;
+//   gate_up at 28 rounds, 10% slower at 4); the queue was 4% slower there,
+//   the partner-group start 3% slower.  Below kSyncMinRounds rounds the
+//   partner-group start (gate_up 8-9% faster than the plain stride at 3-4
+//   rounds);
 // - short-K tiles (down, dx, weight gradients): the queue (down 1-3%, the
 //   backward 3% faster than the plain stride; the rendezvous was slower).
 template <int MODE>
@@ -1171,13 +1214,19 @@ hipError_t launch_mode(int cfg, const GemmKArgs& a, int max_tiles, hipStream_t s
     constexpr int kSched = prefill_sched<MODE>();
     // the backward modes run the 256 x 256 tiles only
     if (cfg == 0 || MODE == kModeWgrad || a_kn<MODE>()) {
-        if (kSched == kSchedQueue || (kSched == kSchedRound && max_tiles >= kSyncMinRounds * num_cus()))
+        if constexpr (kSched == kSchedRound) {
+            if (max_tiles < kSyncMinRounds * num_cus())
+                hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB,
+                                                   kPrefillRowB, kPrefillGM, kSchedGroup, MODE>), dim3(grid), dim3(512),
+                                   0, stream, a);
+            else
+                hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB,
+                                                   kPrefillRowB, kPrefillGM, kSchedRound, MODE>), dim3(grid), dim3(512),
+                                   0, stream, a);
+        } else {
             hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB,
                                                kPrefillRowB, kPrefillGM, kSched, MODE>), dim3(grid), dim3(512), 0, stream, a);
-        else
-            hipLaunchKernelGGL((moe_gemm_kernel<TE, kPrefillBN, 256, 4, 2, kPrefillStagesA, kPrefillStagesB,
-                                               kPrefillRowB, kPrefillGM, kSchedStride, MODE>), dim3(grid), dim3(512), 0,
-                               stream, a);
+        }
     } else if constexpr (!a_kn<MODE>())
         hipLaunchKernelGGL((moe_gemm_kernel<TE, kDecodeBN, 16, 8, 1, kDecodeStages, kDecodeStages, kDecodeRowB, 1, kSchedStride, MODE>), dim3(grid),
                            dim3(512), 0, stream, a);
