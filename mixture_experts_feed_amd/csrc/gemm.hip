@@ -1188,10 +1188,13 @@ constexpr int kPrefillGM = 8;
 //   partner-group start (gate_up 8-9% faster than the plain stride at 3-4
 //   rounds);
 // - short-K tiles (down, dx, weight gradients): the queue (down 1-3%, the
-//   backward 3% faster than the plain stride; the rendezvous was slower).
+//   backward 3% faster than the plain stride; the rendezvous was slower);
+//   for down and dx the partner-group start (another 1.2-1.4% on down).
 template <int MODE>
 constexpr int prefill_sched() {
-    return MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kSchedRound : kSchedQueue;
+    return MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kSchedRound
+           : MODE == kModeDown || MODE == kModeDx                            ? kSchedGroup
+                                                                              : kSchedQueue;
 }
 constexpr int kSyncMinRounds = 8;
 constexpr int kPrefillBN = 256;
