@@ -376,6 +376,26 @@ def main():
                               "TFLOP_s_with_recompute": round((bw_flops + re_flops) / (bms * 1e-3) / 1e12, 2)}
         log(f"[bench] backward {bms:.3f} ms, {btf:.1f} TFLOP/s algorithmic")
 
+        # the same backward with bf16 weight gradients (each the fp32 gradient
+        # rounded once): half the gradient bytes written
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        grads16 = dict(grads, d_w_gu=torch.empty(tuple(inp["w_gu"].shape), **bf),
+                       d_w_d=torch.empty(tuple(inp["w_d"].shape), **bf),
+                       d_wsh_gu=torch.empty(tuple(inp["wsh_gu"].shape), **bf),
+                       d_wsh_d=torch.empty(tuple(inp["wsh_d"].shape), **bf))
+
+        def bw16_call():
+            B.backward(inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"], inp["wsh_gu"], inp["wsh_d"],
+                       w.top_k, w.route_scale, w.global_scale, dout_b, workspace=bws, grads=grads16)
+
+        b16ms, _ = run_timed(torch, B, bw16_call, bw_steps, 2, events)
+        b16tf = bw_flops / (b16ms * 1e-3) / 1e12
+        result["backward_bf16_weight_grads"] = {"workload": w.name, "ms_per_step": round(b16ms, 4),
+                                                "TFLOP_s": round(b16tf, 2),
+                                                "frac_of_peak": round(b16tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] backward, bf16 weight gradients {b16ms:.3f} ms, {b16tf:.1f} TFLOP/s algorithmic")
+        del grads16
+
         # training step: the training forward keeps the gate_up projections,
         # and the backward reads them instead of recomputing
         saved = torch.empty(B.saved_size(bdims), dtype=torch.uint8, device=dev)

@@ -174,14 +174,19 @@ int inkling_moe_forward_train(const inkling_moe_dims_t* dims, const void* x, con
  * expert that receives no token gets zeros.
  *   dout [T][hidden] (dims->dtype);  dx [T][hidden] (dims->out_dtype), which
  *   must alias neither x nor dout.
- * Weight gradients are fp32 with the weights' layouts.
+ * Weight gradients have the weights' layouts.  They are accumulated in fp32
+ * and stored as fp32, or, with weight_grad_dtype = INKLING_BF16, rounded once
+ * to nearest-even bf16 (half the bytes written; each value is the fp32
+ * gradient rounded).  A zero-initialised struct asks for fp32; any other value
+ * returns INKLING_ERR_UNSUPPORTED.  d_gate_bank is always fp32.
  */
 typedef struct {
     float* d_gate_bank;        /* [n_routed + n_shared][hidden] */
-    float* d_routed_gate_up;   /* [n_routed][2*I][hidden]       */
-    float* d_routed_down;      /* [n_routed][hidden][I]         */
-    float* d_shared_gate_up;   /* [n_shared][2*I][hidden] (NULL iff n_shared == 0) */
-    float* d_shared_down;      /* [n_shared][hidden][I]         */
+    void* d_routed_gate_up;    /* [n_routed][2*I][hidden]       */
+    void* d_routed_down;       /* [n_routed][hidden][I]         */
+    void* d_shared_gate_up;    /* [n_shared][2*I][hidden] (NULL iff n_shared == 0) */
+    void* d_shared_down;       /* [n_shared][hidden][I]         */
+    int32_t weight_grad_dtype; /* inkling_dtype_t of the four weight gradients */
 } inkling_moe_grads_t;
 
 int inkling_moe_backward_workspace_size(const inkling_moe_dims_t* dims, size_t* bytes);

@@ -46,7 +46,7 @@ class DenseDims(ctypes.Structure):
 class Grads(ctypes.Structure):
     _fields_ = [("d_gate_bank", ctypes.c_void_p), ("d_routed_gate_up", ctypes.c_void_p),
                 ("d_routed_down", ctypes.c_void_p), ("d_shared_gate_up", ctypes.c_void_p),
-                ("d_shared_down", ctypes.c_void_p)]
+                ("d_shared_down", ctypes.c_void_p), ("weight_grad_dtype", ctypes.c_int32)]
 
 
 class Gate(ctypes.Structure):
@@ -344,10 +344,13 @@ def backward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu:
              wsh_gu: Optional[torch.Tensor], wsh_d: Optional[torch.Tensor], top_k: int, route_scale: float,
              global_scale: float, dout: torch.Tensor, padding_mask: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, dx_dtype: Optional[torch.dtype] = None,
-             grads: Optional[dict] = None, saved: Optional[torch.Tensor] = None) -> dict:
+             grads: Optional[dict] = None, saved: Optional[torch.Tensor] = None,
+             weight_grad_dtype: Optional[torch.dtype] = None) -> dict:
     """inkling_moe_backward: dict(dx, d_gate_bank, d_w_gu, d_w_d, d_wsh_gu, d_wsh_d).
     `saved`: the tensor a training forward with the same arguments filled, or
-    None to recompute the gate_up projections."""
+    None to recompute the gate_up projections.  The weight gradients are fp32
+    (default) or bf16 (`weight_grad_dtype`, or the dtype of the given
+    `grads` tensors)."""
     T, H = x.shape
     E, twoI, _ = w_gu.shape
     S = 0 if wsh_gu is None else wsh_gu.shape[0]
@@ -362,14 +365,20 @@ def backward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu:
     dims = make_dims(T, H, E, top_k, S, twoI // 2, x.dtype, dx_dtype)
     dev = x.device
     if grads is None:
-        f32 = dict(dtype=torch.float32, device=dev)
+        wdt = dict(dtype=torch.float32 if weight_grad_dtype is None else weight_grad_dtype, device=dev)
         grads = {"dx": torch.empty((T, H), dtype=dx_dtype, device=dev),
-                 "d_gate_bank": torch.empty(tuple(gate_bank.shape), **f32),
-                 "d_w_gu": torch.empty(tuple(w_gu.shape), **f32), "d_w_d": torch.empty(tuple(w_d.shape), **f32),
-                 "d_wsh_gu": torch.empty(tuple(wsh_gu.shape), **f32) if S else None,
-                 "d_wsh_d": torch.empty(tuple(wsh_d.shape), **f32) if S else None}
+                 "d_gate_bank": torch.empty(tuple(gate_bank.shape), dtype=torch.float32, device=dev),
+                 "d_w_gu": torch.empty(tuple(w_gu.shape), **wdt), "d_w_d": torch.empty(tuple(w_d.shape), **wdt),
+                 "d_wsh_gu": torch.empty(tuple(wsh_gu.shape), **wdt) if S else None,
+                 "d_wsh_d": torch.empty(tuple(wsh_d.shape), **wdt) if S else None}
+    wdtype = grads["d_w_gu"].dtype
+    if weight_grad_dtype is not None and weight_grad_dtype != wdtype:
+        raise ValueError("weight_grad_dtype differs from the dtype of the given gradient tensors")
+    for n in ("d_w_d", "d_wsh_gu", "d_wsh_d"):
+        if grads[n] is not None and grads[n].dtype != wdtype:
+            raise ValueError("the four weight gradients must share one dtype")
     g = Grads(_ptr(grads["d_gate_bank"]), _ptr(grads["d_w_gu"]), _ptr(grads["d_w_d"]), _ptr(grads["d_wsh_gu"]),
-              _ptr(grads["d_wsh_d"]))
+              _ptr(grads["d_wsh_d"]), _dtype_code(wdtype))
     gate = Gate(gate_bank.data_ptr(), bias.data_ptr(), float(route_scale), float(global_scale))
     ex = Experts(w_gu.data_ptr(), w_d.data_ptr(), _ptr(wsh_gu) if S else None, _ptr(wsh_d) if S else None)
     if padding_mask is not None:

@@ -440,6 +440,7 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     if (g->d_gate_bank == nullptr || g->d_routed_gate_up == nullptr || g->d_routed_down == nullptr ||
         (S > 0 && (g->d_shared_gate_up == nullptr || g->d_shared_down == nullptr)))
         return INKLING_ERR_INVALID_ARGUMENT;
+    if (g->weight_grad_dtype != INKLING_F32 && g->weight_grad_dtype != INKLING_BF16) return INKLING_ERR_UNSUPPORTED;
     if (dx == x || dx == dout) return INKLING_ERR_INVALID_ARGUMENT;
     const BwdLayout B = make_bwd_layout(dims);
     const Layout& L = B.F;
@@ -568,6 +569,7 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     wd.K_s = B.Tpad;
     wd.out_r = g->d_routed_down;
     wd.out_s = g->d_shared_down;
+    wd.out_bf16 = g->weight_grad_dtype == INKLING_BF16 ? 1 : 0;
     wd.counters = p.round_counters + 24;
     HIP_TRY(launch_wgrad(wd, s));
     WgradParams wg = wd;   // d gate_up[e][n][h] = sum_r dh[r][n] x[t(r)][h]

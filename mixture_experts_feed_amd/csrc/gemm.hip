@@ -121,8 +121,9 @@ struct GemmKArgs {
     const void* zero;          // a zero row, at least wg_M elements
     long long a_sh_stride, b_sh_stride;   // element offset of shared problem s in A / B
     int wg_E, wg_M, wg_N, wg_mtiles, wg_ntiles;
-    float* w_out_routed;       // [E][M][N]
-    float* w_out_shared;       // [S][M][N]
+    void* w_out_routed;        // [E][M][N], fp32 or (w_out_bf16) bf16
+    void* w_out_shared;        // [S][M][N]
+    int w_out_bf16;
 };
 
 template <typename TE>
@@ -263,7 +264,7 @@ struct Tile {
     long long segstride;
     const TE* A;
     const TE* B;
-    float* out;          // kModeWgrad: this problem's gradient [M][N]
+    void* out;           // kModeWgrad: this problem's gradient [M][N] (fp32 or bf16)
     int gend;            // end of the tile's partner group (tiles gend - n .. gend - 1)
 };
 
@@ -294,7 +295,7 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
             t.B = reinterpret_cast<const TE*>(a.B_routed) + (size_t)r0 * a.ldb_r;
             t.lda = a.lda_r;
             t.ldb = a.ldb_r;
-            t.out = a.w_out_routed + (size_t)pr * a.wg_M * a.wg_N;
+            t.out = static_cast<char*>(a.w_out_routed) + (size_t)pr * a.wg_M * a.wg_N * (a.w_out_bf16 ? 2 : 4);
         } else {
             const int sx = pr - a.wg_E;
             t.K = a.K_s;
@@ -303,7 +304,7 @@ __device__ __forceinline__ Tile<TE> decode_tile(const GemmKArgs& a, int L, int B
             t.B = reinterpret_cast<const TE*>(a.B_shared) + sx * a.b_sh_stride;
             t.lda = a.lda_s;
             t.ldb = a.ldb_s;
-            t.out = a.w_out_shared + (size_t)sx * a.wg_M * a.wg_N;
+            t.out = static_cast<char*>(a.w_out_shared) + (size_t)sx * a.wg_M * a.wg_N * (a.w_out_bf16 ? 2 : 4);
         }
         t.seg = max(t.K, 1);
         t.segn = t.N;
@@ -1061,8 +1062,27 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                                 (size_t)(cur.is_shared ? cur.t0 : cur.grow0) * cur.N + cur.n0 + wn0;
                     flush_f32(j, mb, [&](int r) -> float* { return hb + (size_t)(mb + r) * cur.N; });
                 } else if constexpr (MODE == kModeWgrad) {
-                    float* hb = cur.out + (size_t)cur.t0 * cur.N + cur.n0 + wn0;
-                    flush_f32(j, mb, [&](int r) -> float* { return hb + (size_t)(mb + r) * cur.N; });
+                    if (a.w_out_bf16) {
+                        // bf16 gradients: the fp32 sums rounded once; 64 columns
+                        // of 2 bytes fill one 128-byte LDS row
+#pragma unroll
+                        for (int i = 0; i < FN; ++i)
+                            if (i < nvi) {
+                                const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                                store4<bf16_t>(reinterpret_cast<bf16_t*>(ep + rw * kEpRowB + (16 * i + 4 * g4) * 2), v4);
+                            }
+                        bf16_t* hb = static_cast<bf16_t*>(cur.out) + (size_t)cur.t0 * cur.N + cur.n0 + wn0;
+#pragma unroll
+                        for (int sgi = 0; sgi < 2; ++sgi) {
+                            const int c = ln + 64 * sgi, r = c >> 3, q = c & 7;
+                            const uint4 d = *reinterpret_cast<const uint4*>(ep + r * kEpRowB + q * 16);
+                            if (mb + r < cur.rows_valid && (q >> 1) < nvi)
+                                *reinterpret_cast<uint4*>(hb + (size_t)(mb + r) * cur.N + 8 * q) = d;
+                        }
+                    } else {
+                        float* hb = static_cast<float*>(cur.out) + (size_t)cur.t0 * cur.N + cur.n0 + wn0;
+                        flush_f32(j, mb, [&](int r) -> float* { return hb + (size_t)(mb + r) * cur.N; });
+                    }
                 } else {
                     // fp32 rows: the layer output is rounded once, in the combine
                     float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) + cur.n0 + wn0;
@@ -1088,7 +1108,7 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             store4<float>(o, w);
                         } else if (MODE == kModeWgrad) {
                             float w[4] = {v[0], v[1], v[2], v[3]};
-                            store4<float>(cur.out + (size_t)(cur.t0 + m) * cur.N + n, w);
+                            store4<float>(static_cast<float*>(cur.out) + (size_t)(cur.t0 + m) * cur.N + n, w);
                         } else if (MODE == kModeGateUp) {
                             // optional fp32 copy of the projection itself (kept for the backward)
                             float* hs = cur.is_shared ? a.h_save_shared : a.h_save_routed;
@@ -1468,6 +1488,7 @@ hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream) {
     a.wg_mtiles = (w.M + 255) / 256;
     a.wg_ntiles = (w.N + kWgradBN - 1) / kWgradBN;
     a.w_out_routed = w.out_r;
+    a.w_out_bf16 = w.out_bf16;
     a.round_counter = w.counters;
     a.w_out_shared = w.out_s;
     const int tiles = (w.E + w.S) * a.wg_mtiles * a.wg_ntiles;

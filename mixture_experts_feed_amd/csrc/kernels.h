@@ -117,8 +117,9 @@ struct WgradParams {
     const void* zero;   // max(M) zeros of the operand type
     int lda_r, ldb_r, lda_s, ldb_s, K_s;
     long long a_sh_stride, b_sh_stride;
-    float* out_r;
-    float* out_s;
+    void* out_r;        // fp32, or bf16 when out_bf16
+    void* out_s;
+    int out_bf16;
     int32_t* counters;   // 8 ints, zero at launch (the tile queue of each XCD)
 };
 hipError_t launch_wgrad(const WgradParams& w, hipStream_t stream);

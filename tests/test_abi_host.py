@@ -197,6 +197,11 @@ def test_backward_argument_checks(lib):
               n.value, None) == B.INKLING_ERR_INVALID_ARGUMENT
     assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, None, dx, ctypes.byref(gr), ws,
               n.value - 1, None) == B.INKLING_ERR_WORKSPACE
+    # weight gradients are fp32 (the zero default) or bf16; nothing else
+    for code in (2, -1):
+        odd = B.Grads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, code)
+        assert bw(ctypes.byref(d), x, ctypes.byref(gate), ctypes.byref(ex), None, dout, None, dx, ctypes.byref(odd),
+                  ws, n.value, None) == B.INKLING_ERR_UNSUPPORTED
     bad = _dims(hidden=96)
     assert lib.inkling_moe_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == B.INKLING_ERR_UNSUPPORTED
 

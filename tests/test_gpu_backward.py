@@ -201,3 +201,38 @@ def test_training_forward_and_saved_backward(name):
         if g_re[k] is not None:
             assert torch.equal(g_re[k], g_sv[k]), f"{k} differs between saved and recomputed projections"
     _say(f"[saved] {name} ok: forward and every gradient bit-identical")
+
+
+BF16_GRAD_CASES = {
+    "ragged_bf16": CASES["ragged_bf16"],
+    "f32_many_rows": CASES["f32_many_rows"],
+    "few_rows_empty_experts": CASES["few_rows_empty_experts"],
+    "no_shared": CASES["no_shared"],
+    "prefill_h6144": wl.WORKLOADS["prefill_h6144"],
+}
+
+
+@pytest.mark.parametrize("name", list(BF16_GRAD_CASES))
+def test_bf16_weight_gradients_are_the_rounded_fp32_ones(name):
+    """weight_grad_dtype = bf16 stores each weight gradient as its fp32 value
+    rounded to nearest-even, bit for bit; dx and the gate-bank gradient do not
+    change.  (The fp32 gradients are the ones compared with the oracle.)"""
+    w = BF16_GRAD_CASES[name]
+    _say(f"[bf16 grads] {w}")
+    inp = wl.make_inputs(w, device=DEV)
+    S = w.n_shared
+    args = (inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"], inp["wsh_gu"] if S else None,
+            inp["wsh_d"] if S else None, w.top_k, inp["route_scale"], inp["global_scale"])
+    dout = _dout(w)
+    g32 = B.backward(*args, dout)
+    g16 = B.backward(*args, dout, weight_grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in ("d_w_gu", "d_w_d", "d_wsh_gu", "d_wsh_d"):
+        if g32[k] is None:
+            assert g16[k] is None
+            continue
+        assert g16[k].dtype == torch.bfloat16
+        assert torch.equal(g16[k], g32[k].to(torch.bfloat16)), f"{k}: bf16 gradient is not the rounded fp32 one"
+    for k in ("dx", "d_gate_bank"):
+        assert torch.equal(g16[k], g32[k]), k
+    _say(f"[bf16 grads] {name} ok")
