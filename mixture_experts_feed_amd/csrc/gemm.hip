@@ -528,10 +528,13 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
     };
     // kSchedGroup: before a tile's K loop, thread 0 waits until the counter
     // has handed out every partner tile of its range (the K loop's first
-    // barrier holds the other threads)
+    // barrier holds the other threads).  Partners beyond L + nloc - 1 are not
+    // waited for: with at most nloc workgroups, a wait for more could only end
+    // at the poll limit, while up to L + nloc - 1 the tiles held by waiting
+    // workgroups always cover it.
     auto group_wait = [&](const Tile<TE>& t) __attribute__((always_inline)) {
         if constexpr (SCHED == kSchedGroup) {
-            const int need = min(t.gend, L_end) - (L_beg + nloc);   // counter value that covers the group
+            const int need = min(min(t.gend, L_end), L + nloc) - (L_beg + nloc);   // counter value that covers it
             if (tid == 0 && need > 0)
                 for (int it = 0; it < kSpinLimit; ++it) {
                     if (__hip_atomic_load(a.round_counter + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need)

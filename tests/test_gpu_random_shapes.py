@@ -6,8 +6,9 @@ both operand types and with and without a padding mask, so the launch
 configurations (tile counts, ragged tails, schedules below and above one
 round of tiles) vary from case to case.  Each case is compared element by
 element with the fp64 oracle under the same bars as the other parity tests.
-One more case gives experts thousands of rows (about 32 row tiles each), so
-that the row tiles sharing a weight tile outnumber a start group.
+One more case gives experts thousands of rows (16 row tiles each), so that
+the row tiles sharing a weight tile outnumber a start group, and one has
+start groups larger than the workgroups of an XCD.
 """
 import sys
 
@@ -41,9 +42,12 @@ def _draw_cases(n=10, seed=20261203):
         name = (f"r{c}_T{kw['T']}_H{kw['hidden']}_E{E}_k{k}_S{S}_I{kw['intermediate']}_{kw['dtype']}"
                 f"{'_pad' if mask_frac else ''}")
         cases[name] = (wl.custom(name=name, **kw), mask_frac)
-    # experts of about 8000 rows: 32 row tiles per weight tile
+    # experts of 4096 rows: 16 row tiles per weight tile
     w = wl.custom(name="big_experts", T=4096, hidden=128, n_routed=4, top_k=4, n_shared=1, intermediate=64)
     cases["big_experts_T4096_E4_k4"] = (w, 0.0)
+    # nine tiles in all, two workgroups per XCD, start groups of eight row tiles
+    w = wl.custom(name="few_workgroups", T=2048, hidden=64, n_routed=1, top_k=1, n_shared=1, intermediate=64)
+    cases["few_workgroups_T2048_E1"] = (w, 0.0)
     return cases
 
 
