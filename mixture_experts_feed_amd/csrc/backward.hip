@@ -182,8 +182,10 @@ constexpr int kBankJW = 3;       // 16-row blocks of the bank per wave
 // fp32 matrix cores (x widened exactly, products and sums in fp32); grid
 // (H/64, ceil(NE/(16*kBankJW)), kBankSplit), one wave of 48 bank rows x 64
 // hidden columns.  MFMA operands come straight from global memory: lane l
-// holds dz[t + l/16][j0 + l%16] (A, rows = bank rows) and x[t + l/16][h0 + l%16]
-// (B, columns = hidden), four tokens per step in ascending order.
+// holds dz[t + l/16][j0 + l%16] (A, rows = bank rows) and, for the MFMA of
+// column block v, x[t + l/16][h0 + 4(l%16) + v] (B, columns = hidden): a lane's
+// four B values are one 8- or 16-byte load.  Four tokens per step, in
+// ascending order.
 template <typename TX>
 __global__ __launch_bounds__(64) void dbank_partial_kernel(const float* __restrict__ dz, const TX* __restrict__ x,
                                                            int T, int H, int NE, float* __restrict__ part) {
@@ -206,24 +208,39 @@ __global__ __launch_bounds__(64) void dbank_partial_kernel(const float* __restri
             const int j = (jb0 + u) * 16 + cl;
             a[u] = (tv && j < NE) ? dz[(size_t)tt * NE + j] : 0.f;
         }
+        if (tv) {
+            const TX* xp = x + (size_t)tt * H + h0 + 4 * cl;
+            if constexpr (sizeof(TX) == 2) {
+                const uint2 q = *reinterpret_cast<const uint2*>(xp);
+                b[0] = __uint_as_float(q.x << 16);
+                b[1] = __uint_as_float(q.x & 0xFFFF0000u);
+                b[2] = __uint_as_float(q.y << 16);
+                b[3] = __uint_as_float(q.y & 0xFFFF0000u);
+            } else {
+                const float4 q = *reinterpret_cast<const float4*>(xp);
+                b[0] = q.x;
+                b[1] = q.y;
+                b[2] = q.z;
+                b[3] = q.w;
+            }
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) b[v] = tv ? to_f32<TX>(x[(size_t)tt * H + h0 + 16 * v + cl]) : 0.f;
+            for (int v = 0; v < 4; ++v) b[v] = 0.f;
+        }
 #pragma unroll
         for (int u = 0; u < kBankJW; ++u)
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[v], acc[u][v], 0, 0, 0);
     }
-    // lane l holds rows j0 + 4(l/16) + r, column h0 + l%16 of each 16x16 block
+    // lane l holds rows j0 + 4(l/16) + r, columns h0 + 4(l%16) + v (v = block)
 #pragma unroll
     for (int u = 0; u < kBankJW; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j = (jb0 + u) * 16 + 4 * kr + r;
-            if (j < NE) {
-                float* o = part + ((size_t)blockIdx.z * NE + j) * H + h0 + cl;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) o[16 * v] = acc[u][v][r];
-            }
+            if (j < NE)
+                *reinterpret_cast<float4*>(part + ((size_t)blockIdx.z * NE + j) * H + h0 + 4 * cl) =
+                    make_float4(acc[u][0][r], acc[u][1][r], acc[u][2][r], acc[u][3][r]);
         }
 }
 
