@@ -96,7 +96,7 @@ struct GemmKArgs {
     int seg_s;              // shared A(n, kk) = A_shared + (kk/seg)*N_s*seg + n*seg + kk%seg
     int shared_blocks, shared_mtiles;
     int has_routed;
-    int32_t* round_counter;    // [8] per XCD, zero at launch: tiles finished (kSchedRound) or taken (kSchedQueue)
+    int32_t* round_counter;    // [8] per XCD, zero at launch: tiles finished (kSchedRound) or taken (queue, group)
     // kModeDAct
     const void* h_routed;      // [T*k][2I] sorted rows, fp32
     const void* h_shared;      // [T][S*2I] fp32
