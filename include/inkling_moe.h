@@ -146,10 +146,12 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
 /*
  * Training forward: inkling_moe_forward (same out, bit for bit) that also
  * keeps, for inkling_moe_backward, the gate_up projections h = gate_up(x) in
- * fp32, the interleaved [gate, up] columns of each row:
- *   saved = [T*top_k][2*I] for the routed rows, in the expert-sorted order of
- *           the routing (rows past the routed count unused), then
- *           [T][n_shared*2*I] for the shared experts;
+ * fp32, the interleaved [gate, up] columns of each row, and the gate logits:
+ *   saved = [T*top_k][2*I] fp32 for the routed rows, in the expert-sorted
+ *           order of the routing (rows past the routed count unused), then
+ *           [T][n_shared*2*I] fp32 for the shared experts, then
+ *           [T][n_routed + n_shared] fp64 logits (the backward routes from
+ *           them instead of recomputing them, with the same result);
  * inkling_moe_saved_size gives its size in bytes.  The caller owns `saved`
  * (device memory), and it stays valid for a backward with the same dims,
  * inputs, gate, experts and padding_mask.  The pages' layer is trained by

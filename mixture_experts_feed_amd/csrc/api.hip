@@ -120,13 +120,24 @@ struct RouteBufs {
     int32_t* num_tiles;
 };
 
+// z_out: also write the summed logits [T][E+S] there (the training forward);
+// z_in: take the logits from there instead of computing them (the backward
+// from a training forward's saved buffer: the same sums, so the same routing)
 int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const inkling_gate_t* g,
-              const uint8_t* pad, const RouteBufs& rb, bool permute, void* ws, hipStream_t s) {
+              const uint8_t* pad, const RouteBufs& rb, bool permute, void* ws, hipStream_t s,
+              double* z_out = nullptr, const double* z_in = nullptr) {
     const int T = (int)d->T, E = d->n_routed, S = d->n_shared, k = d->top_k, H = d->hidden;
-    double* zpart = at<double>(ws, L.zpart);
-    HIP_TRY(launch_router_logits(d->dtype, x, g->gate_bank, zpart, T, H, E + S, L.ksplit, s));
+    const double* zp = z_in;
+    int ks = 1;
+    if (z_in == nullptr) {
+        double* zpart = at<double>(ws, L.zpart);
+        HIP_TRY(launch_router_logits(d->dtype, x, g->gate_bank, zpart, T, H, E + S, L.ksplit, s));
+        if (z_out != nullptr) HIP_TRY(launch_logits_sum(zpart, L.ksplit, T, E + S, z_out, s));
+        zp = zpart;
+        ks = L.ksplit;
+    }
     HIP_TRY(mark(1, s));
-    HIP_TRY(launch_router_select(zpart, L.ksplit, g->correction_bias, T, E, S, k, g->route_scale, g->global_scale,
+    HIP_TRY(launch_router_select(zp, ks, g->correction_bias, T, E, S, k, g->route_scale, g->global_scale,
                                  rb.topk_idx, rb.topk_w, rb.shared_g, s));
     HIP_TRY(mark(2, s));
     if (!permute) return INKLING_OK;
@@ -263,6 +274,19 @@ namespace {
 
 // the forward; with `saved`, the gate_up projections are also written there
 // (fp32: routed rows [T*k][2I] in expert-sorted order, then shared [T][S*2I])
+// saved buffer of the training forward: the gate_up projections h (fp32,
+// [T*k][2I] by expert-sorted row, then [T][S*2I]), then the gate logits z
+// (fp64, [T][E+S])
+size_t saved_h_bytes(const inkling_moe_dims_t* d) {
+    return (size_t)d->T * (size_t)(d->top_k + d->n_shared) * 2 * (size_t)d->intermediate * sizeof(float);
+}
+size_t saved_bytes(const inkling_moe_dims_t* d) {
+    return saved_h_bytes(d) + (size_t)d->T * (size_t)(d->n_routed + d->n_shared) * sizeof(double);
+}
+double* saved_logits(const inkling_moe_dims_t* d, const void* saved) {
+    return reinterpret_cast<double*>(static_cast<char*>(const_cast<void*>(saved)) + saved_h_bytes(d));
+}
+
 int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
                  const inkling_experts_t* w, const uint8_t* padding_mask, void* out, inkling_route_out_t* r,
                  void* saved, void* workspace, size_t workspace_bytes, void* stream) {
@@ -291,7 +315,8 @@ int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_ga
     rb.tiles = at<RoutedTile>(workspace, L.tiles);
     rb.num_tiles = at<int32_t>(workspace, L.num_tiles);
     HIP_TRY(mark(0, s));
-    rc = run_route(dims, L, x, gate, padding_mask, rb, true, workspace, s);
+    rc = run_route(dims, L, x, gate, padding_mask, rb, true, workspace, s,
+                   saved != nullptr ? saved_logits(dims, saved) : nullptr);
     if (rc != INKLING_OK) return rc;
 
     MoeGemmParams p = {};
@@ -338,9 +363,6 @@ int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_ga
     return INKLING_OK;
 }
 
-size_t saved_bytes(const inkling_moe_dims_t* d) {
-    return (size_t)d->T * (size_t)(d->top_k + d->n_shared) * 2 * (size_t)d->intermediate * sizeof(float);
-}
 
 }  // namespace
 
@@ -462,7 +484,9 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     rb.pos = at<int32_t>(workspace, L.pos);
     rb.tiles = at<RoutedTile>(workspace, L.tiles);
     rb.num_tiles = at<int32_t>(workspace, L.num_tiles);
-    rc = run_route(dims, L, x, gate, padding_mask, rb, true, workspace, s);
+    // routing: from the training forward's logits when they were kept
+    const double* z_kept = saved != nullptr ? saved_logits(dims, saved) : nullptr;
+    rc = run_route(dims, L, x, gate, padding_mask, rb, true, workspace, s, nullptr, z_kept);
     if (rc != INKLING_OK) return rc;
     int32_t* poff = at<int32_t>(workspace, B.poff);
     HIP_TRY(launch_padded_offsets(rb.counts, E, poff, s));
@@ -525,7 +549,8 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     // 4. gate: dz of the selected and shared logits
     float* dz = at<float>(workspace, B.dz);
     float* dzc = at<float>(workspace, B.dzc);
-    HIP_TRY(launch_router_backward(at<double>(workspace, L.zpart), L.ksplit, rb.topk_idx, rb.pos, ab.dgp_r, ab.dgp_sh,
+    HIP_TRY(launch_router_backward(z_kept != nullptr ? z_kept : at<double>(workspace, L.zpart),
+                                   z_kept != nullptr ? 1 : L.ksplit, rb.topk_idx, rb.pos, ab.dgp_r, ab.dgp_sh,
                                    T, E, S, k, I, gate->route_scale, gate->global_scale, dz, dzc, s));
 
     // 5. dx rows: the gate_up projections against dh (the down-GEMM shape,

@@ -17,6 +17,9 @@ hipError_t launch_router_select(const double* zpart, int ksplit, const float* bi
                                 float route_scale, float global_scale, int32_t* topk_idx, float* topk_w,
                                 float* shared_g, hipStream_t stream);
 int router_ksplit(int T, int H, int NE);
+// z[T][NE] = the partial logits summed over the ksplit slices, in slice order
+// (read back with ksplit = 1, they give the same sums bit for bit)
+hipError_t launch_logits_sum(const double* zpart, int ksplit, int T, int NE, double* z, hipStream_t stream);
 
 // ---- permutation (permute.hip) -------------------------------------------
 hipError_t launch_build_masks(const int32_t* topk_idx, const uint8_t* pad, int T, int E, int k, uint64_t* masks,

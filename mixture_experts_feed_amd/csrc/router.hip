@@ -273,7 +273,26 @@ __global__ __launch_bounds__(256) void router_select_kernel(const double* __rest
     }
 }
 
+// z[i] = the partial logits of element i summed over the slices in slice
+// order, from 0.0 (the order router_select_kernel and the router backward
+// sum them in, so either reads the same values from z with one slice)
+__global__ __launch_bounds__(256) void zsum_kernel(const double* __restrict__ zpart, int ksplit, size_t n,
+                                                   double* __restrict__ z) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    double s = 0.0;
+    for (int p = 0; p < ksplit; ++p) s += zpart[(size_t)p * n + i];
+    z[i] = s;
+}
+
 }  // namespace
+
+hipError_t launch_logits_sum(const double* zpart, int ksplit, int T, int NE, double* z, hipStream_t stream) {
+    const size_t n = (size_t)T * NE;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(zsum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, zpart, ksplit, n, z);
+    return hipGetLastError();
+}
 
 int router_ksplit(int T, int H, int NE) {
     const int tok = router_tok_tile(T);

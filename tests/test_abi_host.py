@@ -207,12 +207,12 @@ def test_backward_argument_checks(lib):
 
 
 def test_training_forward_argument_checks(lib):
-    """saved_size = (T*top_k + T*n_shared) * 2I fp32; the training forward needs
+    """saved_size = (T*top_k + T*n_shared) * 2I fp32 + T*(E+S) fp64; the training forward needs
     its saved buffer and checks its other arguments as the forward does."""
     d = _dims()
     n = ctypes.c_size_t(0)
     assert lib.inkling_moe_saved_size(ctypes.byref(d), ctypes.byref(n)) == B.INKLING_OK
-    assert n.value == d.T * (d.top_k + d.n_shared) * 2 * d.intermediate * 4
+    assert n.value == d.T * (d.top_k + d.n_shared) * 2 * d.intermediate * 4 + d.T * (d.n_routed + d.n_shared) * 8
     assert lib.inkling_moe_saved_size(ctypes.byref(d), None) == B.INKLING_ERR_INVALID_ARGUMENT
     bad = _dims(hidden=96)
     assert lib.inkling_moe_saved_size(ctypes.byref(bad), ctypes.byref(n)) == B.INKLING_ERR_UNSUPPORTED
