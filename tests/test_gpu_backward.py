@@ -62,7 +62,7 @@ def _close_wgrad(name, gpu, ref, absref, dtype):
     excess = np.abs(g - ref) - ABS_BOUND * np.asarray(absref) - 1e-6 * rms
     worst = float(np.max(np.abs(g - ref) / (np.asarray(absref) + 1e-30 * rms + 1e-300)))
     _say(f"[backward]   {name}: max |err| / sum|u v| = {worst:.2e} (bound {ABS_BOUND:.2e}), "
-         f"max_err/rms={float(np.max(np.abs(g - ref))) / rms:.2e}")
+         f"max_err/rms={float(np.max(np.abs(g - ref))) / rms if rms > 0 else 0.0:.2e}")
     assert np.all(excess <= 0), f"{name}: {int(np.sum(excess > 0))} elements above the bound"
     return worst
 
@@ -120,6 +120,21 @@ def test_backward_padding_mask():
     g = torch.Generator().manual_seed(11)
     mask = (torch.rand((w.T,), generator=g) < 0.3).to(torch.uint8).to(DEV)
     _full_backward(w, padding_mask=mask)
+
+
+@pytest.mark.parametrize("S", [2, 0])
+def test_backward_every_token_padded(S):
+    """No routed rows: the routed weight gradients are exact zeros, and without
+    shared experts so are dx and the gate-bank gradient."""
+    w = CASES["ragged_bf16"]
+    if S != w.n_shared:
+        w = wl.custom(T=w.T, hidden=w.hidden, n_routed=w.n_routed, top_k=w.top_k, n_shared=S,
+                      intermediate=w.intermediate)
+    mask = torch.ones((w.T,), dtype=torch.uint8, device=DEV)
+    g = _full_backward(w, padding_mask=mask)
+    assert not bool(g["d_w_gu"].any()) and not bool(g["d_w_d"].any())
+    if S == 0:
+        assert not bool(g["dx"].any()) and not bool(g["d_gate_bank"].any())
 
 
 def test_backward_small_bf16():

@@ -112,6 +112,24 @@ def test_padding_mask():
     assert counts.sum() == int((mask == 0).sum()) * w.top_k
 
 
+EVERY_TOKEN_PADDED = {
+    "T200_S2": EDGE["ragged_bf16"],
+    # 40 tokens take the one-workgroup permutation; no shared experts: the output is zero
+    "T40_S0": wl.custom(T=40, hidden=128, n_routed=8, top_k=2, n_shared=0, intermediate=64),
+}
+
+
+@pytest.mark.parametrize("name", list(EVERY_TOKEN_PADDED))
+def test_every_token_padded(name):
+    """No routed rows at all: every expert is empty and only the shared experts run."""
+    w = EVERY_TOKEN_PADDED[name]
+    mask = torch.ones((w.T,), dtype=torch.uint8, device=DEV)
+    out, routing = _full_parity(w, padding_mask=mask)
+    assert int(routing["expert_counts"].sum()) == 0
+    if w.n_shared == 0:
+        assert not bool(out.any())
+
+
 def test_forced_ties_lower_index_wins():
     """Duplicated gate rows with zero bias tie exactly; the lower index must win."""
     w = wl.custom(T=64, hidden=128, n_routed=8, top_k=2, n_shared=1, intermediate=64)
