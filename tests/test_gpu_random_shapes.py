@@ -8,7 +8,8 @@ round of tiles) vary from case to case.  Each case is compared element by
 element with the fp64 oracle under the same bars as the other parity tests.
 One more case gives experts thousands of rows (16 row tiles each), so that
 the row tiles sharing a weight tile outnumber a start group, and one has
-start groups larger than the workgroups of an XCD.
+start groups larger than the workgroups of an XCD.  The backward is checked
+on the same shapes.
 """
 import sys
 
@@ -83,3 +84,17 @@ def test_random_shape(name):
                                   w.top_k, w.route_scale, w.global_scale, padding_mask=pm, routing=ref)
     rel = P.check_output(out, o_ref, w.dtype)
     _say(f"[random] ok: band={band} max_err/rms={rel:.2e}")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_random_shape_backward(name):
+    """The backward on the same shapes: dx, the gate-bank gradient and every
+    weight gradient against the oracle's, under the backward's bars."""
+    from tests.test_gpu_backward import _full_backward
+    w, mask_frac = CASES[name]
+    _say(f"[random backward] {name}")
+    mask = None
+    if mask_frac > 0:
+        g = torch.Generator().manual_seed(w.T)
+        mask = (torch.rand((w.T,), generator=g) < mask_frac).to(torch.uint8).to(DEV)
+    _full_backward(w, padding_mask=mask)
