@@ -193,13 +193,17 @@ def test_training_forward_and_saved_backward(name):
     backward from its saved projections gives the recomputing backward's
     gradients bit for bit (same routing, same GEMM K order)."""
     w = SAVED_CASES[name]
-    _say(f"[saved] {w}")
-    inp = wl.make_inputs(w, device=DEV)
-    S = w.n_shared
     g = torch.Generator().manual_seed(11)
     mask = None
     if name == "ragged_bf16":
         mask = (torch.rand((w.T,), generator=g) < 0.3).to(torch.uint8).to(DEV)
+    saved_vs_recompute(name, w, mask)
+
+
+def saved_vs_recompute(name, w, mask):
+    _say(f"[saved] {w}")
+    inp = wl.make_inputs(w, device=DEV)
+    S = w.n_shared
     args = (inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"], inp["wsh_gu"] if S else None,
             inp["wsh_d"] if S else None, w.top_k, inp["route_scale"], inp["global_scale"])
     dims = B.make_dims(w.T, w.hidden, w.n_routed, w.top_k, S, w.intermediate, w.torch_dtype)

@@ -8,7 +8,8 @@ round of tiles) vary from case to case.  Each case is compared element by
 element with the fp64 oracle under the same bars as the other parity tests.
 One more case gives experts thousands of rows (16 row tiles each), so that
 the row tiles sharing a weight tile outnumber a start group, and one has
-start groups larger than the workgroups of an XCD.  The backward is checked
+start groups larger than the workgroups of an XCD.  The backward, and the
+training forward with the backward from its saved projections, are checked
 on the same shapes.
 """
 import sys
@@ -98,3 +99,17 @@ def test_random_shape_backward(name):
         g = torch.Generator().manual_seed(w.T)
         mask = (torch.rand((w.T,), generator=g) < mask_frac).to(torch.uint8).to(DEV)
     _full_backward(w, padding_mask=mask)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_random_shape_saved_backward(name):
+    """The training forward and the backward from its saved projections on the
+    same shapes: output and every gradient bit-identical to the forward's and
+    the recomputing backward's."""
+    from tests.test_gpu_backward import saved_vs_recompute
+    w, mask_frac = CASES[name]
+    mask = None
+    if mask_frac > 0:
+        g = torch.Generator().manual_seed(w.T)
+        mask = (torch.rand((w.T,), generator=g) < mask_frac).to(torch.uint8).to(DEV)
+    saved_vs_recompute(name, w, mask)
