@@ -9,6 +9,9 @@ namespace inkling {
 typedef uint16_t bf16_t;  // storage type of bfloat16 values
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16_t;  // IEEE half: the activation between the two expert projections of a bf16 layer
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 

@@ -143,6 +143,38 @@ __device__ __forceinline__ void mma16<float>(f32x4_t& acc, const uint4& a, const
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
+// The activation between the two projections of a bf16 layer is kept in fp16,
+// not bf16: act = gamma silu(g) u is rounded once before the down projection,
+// and fp16's 11-bit significand makes that rounding 8x smaller than bf16's.
+// (On heavy-tailed inputs, where rows of 4x the norm give outputs far above the
+// RMS, the bf16 rounding alone reaches about 2.6e-2 of the output RMS; fp16
+// gives about 3e-3.)  The down weights stay bf16 in memory and are converted to
+// fp16 as MFMA fragments, which is exact for every bf16 value with
+// 2^-17 <= |w| < 2^16 (smaller ones truncate to the fp16 subnormal grid,
+// an error below 2^-24); act must stay below 65504 in magnitude.
+template <typename TE>
+struct ActOf {
+    using type = TE;
+};
+template <>
+struct ActOf<bf16_t> {
+    using type = f16_t;
+};
+
+__device__ __forceinline__ void mma16_f16(f32x4_t& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc,
+                                                 0, 0, 0);
+}
+
+// eight bf16 -> eight fp16 (two per v_cvt_pkrtz_f16_f32; exact in fp16's range)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)));
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
+    return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+}
+
 // sigmoid through the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an
 // IEEE division sequence; exp overflow gives 1/inf = 0, the right limit
 __device__ __forceinline__ float sigmoid(float v) { return __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
@@ -171,6 +203,11 @@ __device__ __forceinline__ void store2<bf16_t>(bf16_t* p, float a, float b) {
 template <>
 __device__ __forceinline__ void store2<float>(float* p, float a, float b) {
     *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+template <>
+__device__ __forceinline__ void store2<f16_t>(f16_t* p, float a, float b) {
+    const f16x2_t v = {(f16_t)a, (f16_t)b};   // round to nearest even (v_cvt_pk_f16_f32)
+    *reinterpret_cast<f16x2_t*>(p) = v;
 }
 
 template <typename TE>
@@ -417,6 +454,10 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
     // operands read as [K][N]: a stage holds BK rows of K, each the tile's BN
     // (A) or BM (B) columns, filled by the same number of 1 KB wave loads
     constexpr bool AKN = a_kn<MODE>(), BKN = b_kn<MODE>();
+    // activation rows (written by gate_up, read by down): fp16 for bf16 layers,
+    // so the bf16 down weights are converted to fp16 fragments (f16 MFMA)
+    using TA = typename ActOf<TE>::type;
+    constexpr bool CVT = MODE == kModeDown && std::is_same<TE, bf16_t>::value;
     constexpr int RBA = BN * (int)sizeof(TE), RBB = BM * (int)sizeof(TE);   // bytes per K row
     constexpr int CHA = RBA / 16, CHB = RBB / 16;                           // 16-byte chunks per K row
     constexpr int RPIA = 1024 / RBA, RPIB = 1024 / RBB;                     // K rows per wave load
@@ -866,10 +907,23 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                         }
                         __builtin_amdgcn_sched_barrier(0);
                         constexpr int jbase = half ? H1 : 0, jn = half ? H2 : H1;
+                        if constexpr (CVT) {
+                            // bf16 weight fragments -> fp16, once per k-step (at
+                            // its first half-step, after the wait above)
+                            if constexpr (half == 0) {
 #pragma unroll
-                        for (int j = 0; j < jn; ++j)
+                                for (int i = 0; i < FN; ++i) fa[acur][i] = bf16x8_to_f16x8(fa[acur][i]);
+                            }
 #pragma unroll
-                            for (int i = 0; i < FN; ++i) mma16<TE>(acc[i][jbase + j], fa[acur][i], fb[bcur][j]);
+                            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                                for (int j = 0; j < jn; ++j) mma16_f16(acc[i][jbase + j], fa[acur][i], fb[bcur][j]);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < jn; ++j)
+#pragma unroll
+                                for (int i = 0; i < FN; ++i) mma16<TE>(acc[i][jbase + j], fa[acur][i], fb[bcur][j]);
+                        }
                         __builtin_amdgcn_sched_barrier(0);
                     });
                 }
@@ -1038,19 +1092,19 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             const f32x4_t v = acc[i][j];
                             const int n = cur.n0 + wn0 + 16 * i + 4 * g4;
                             const float g = cur.is_shared && n / (2 * a.I) != ep_s0 ? g1 : g0;
-                            store2<TE>(reinterpret_cast<TE*>(ep + rw * kEpRowB + (8 * i + 2 * g4) * sizeof(TE)),
+                            store2<TA>(reinterpret_cast<TA*>(ep + rw * kEpRowB + (8 * i + 2 * g4) * sizeof(TA)),
                                        silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
                         }
                     }
-                    constexpr int CPR = 32 * (int)sizeof(TE) / 16;   // 16-byte chunks per row
+                    constexpr int CPR = 32 * (int)sizeof(TA) / 16;   // 16-byte chunks per row
                     const int ld = cur.is_shared ? a.S * a.I : a.I;
-                    TE* obase = reinterpret_cast<TE*>(cur.is_shared ? a.out_shared : a.out_routed) +
+                    TA* obase = reinterpret_cast<TA*>(cur.is_shared ? a.out_shared : a.out_routed) +
                                 (size_t)(cur.is_shared ? cur.t0 : cur.grow0) * ld + ((cur.n0 + wn0) >> 1);
 #pragma unroll
                     for (int sgi = 0; sgi < 16 * CPR / 64; ++sgi) {
                         const int c = ln + 64 * sgi, r = c / CPR, q = c % CPR;
                         const uint4 d = *reinterpret_cast<const uint4*>(ep + r * kEpRowB + q * 16);
-                        const int col = q * (16 / (int)sizeof(TE));
+                        const int col = q * (16 / (int)sizeof(TA));
                         if (mb + r < cur.rows_valid && col / 8 < nvi)
                             *reinterpret_cast<uint4*>(obase + (size_t)(mb + r) * ld + col) = d;
                     }
@@ -1118,14 +1172,14 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             if (cur.is_shared) {
                                 const int t = cur.t0 + m;
                                 const float g = (n / (2 * a.I) == ep_s0) ? ep_g0[j] : ep_g1[j];
-                                TE* o = reinterpret_cast<TE*>(a.out_shared) + (size_t)t * a.S * a.I + (n >> 1);
-                                store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
+                                TA* o = reinterpret_cast<TA*>(a.out_shared) + (size_t)t * a.S * a.I + (n >> 1);
+                                store2<TA>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
                                 if (hs != nullptr) hs += (size_t)t * cur.N + n;
                             } else {
                                 const int row = cur.grow0 + m;
                                 const float g = ep_g0[j];
-                                TE* o = reinterpret_cast<TE*>(a.out_routed) + (size_t)row * a.I + (n >> 1);
-                                store2<TE>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
+                                TA* o = reinterpret_cast<TA*>(a.out_routed) + (size_t)row * a.I + (n >> 1);
+                                store2<TA>(o, silu(v[0]) * v[1] * g, silu(v[2]) * v[3] * g);
                                 if (hs != nullptr) hs += (size_t)row * cur.N + n;
                             }
                             if (hs != nullptr) {

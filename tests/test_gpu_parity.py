@@ -1,9 +1,10 @@
 """GPU parity of the HIP path against the fp64 CPU oracle, through the C ABI.
 
-Small workloads compare every output element; the hidden=6144 workloads
-(prefill T=8192, decode T=32, skewed T=16384) compare the full routing of every
-token and the outputs of sampled tokens, in the same launch configuration the
-benchmark times.
+Every workload compares every output element with the oracle (the hidden=6144
+ones -- prefill T=8192, decode T=32, skewed T=16384, the expert-parallel shard
+and Inkling's default shape -- in the launch configuration the benchmark
+times), and the full routing of every token.  Only the T=65536 case and the
+dense MLP at hidden 6144 compare sampled tokens.
 """
 import sys
 
@@ -168,7 +169,12 @@ def h6144_experts():
     return wl.expert_weights(w, device=DEV)
 
 
-def _sampled_parity(name, experts, n_sample=24):
+def _h6144_parity(name, experts):
+    """Full-size workload in the benchmark's launch configuration: routing of
+    every token bit-exact, and the fp32 output of every token compared with the
+    oracle over all T x hidden elements (max error and RMS over the whole
+    output).  The largest-norm rows of a workload with outlier rows are also
+    reported on their own."""
     w = wl.WORKLOADS[name]
     _say(f"[parity] {name}: T={w.T}")
     inp = wl.make_inputs(w, device=DEV, with_experts=False)
@@ -176,19 +182,21 @@ def _sampled_parity(name, experts, n_sample=24):
     out, routing = _run_both(w, inp)
     ref = P.oracle_route(inp, w.top_k)
     band = P.check_routing(routing, ref, w.top_k)
-    rng = np.random.default_rng(1)
-    T = w.T
-    rows = sorted(set([0, 1, T - 2, T - 1] + rng.choice(T, size=min(T, n_sample), replace=False).tolist()))
-    if w.x_outlier is not None:
-        norms = inp["x"].float().norm(dim=1).cpu().numpy()
-        rows = sorted(set(rows) | set(np.argsort(-norms)[:6].tolist()))
+    _say(f"[parity] {name}: routing ok (band={band}); oracle output of all {w.T} tokens")
     o_ref, _ = oracle.moe_forward(P.host(inp["x"]), P.host(inp["gate_bank"]), P.host(inp["bias"]),
                                   P.HostExperts(inp["w_gu"]), P.HostExperts(inp["w_d"]),
                                   P.HostExperts(inp["wsh_gu"]), P.HostExperts(inp["wsh_d"]),
-                                  w.top_k, w.route_scale, w.global_scale, tokens=rows, routing=ref)
-    rel = P.check_output(out, o_ref, w.dtype, rows=rows)
+                                  w.top_k, w.route_scale, w.global_scale, routing=ref)
+    rel = P.check_output(out, o_ref, w.dtype)
+    extra = ""
+    if w.x_outlier is not None:
+        norms = inp["x"].float().norm(dim=1).cpu().numpy()
+        top = np.argsort(-norms)[:6]
+        g = out.float().cpu().numpy().astype(np.float64)[top]
+        rms = float(np.sqrt(np.mean(o_ref ** 2)))
+        extra = f" largest-norm rows max_err/rms={float(np.max(np.abs(g - o_ref[top]))) / rms:.2e}"
     counts = routing["expert_counts"].cpu().numpy()
-    _say(f"[parity] {name} ok: band={band} rows={len(rows)} max_err/rms={rel:.2e} "
+    _say(f"[parity] {name} ok: band={band} all {w.T}x{w.hidden} elements max_err/rms={rel:.2e}{extra} "
          f"empty={int((counts == 0).sum())} max_count={int(counts.max())}")
 
 
@@ -213,15 +221,15 @@ def test_large_token_count_T65536():
 
 
 def test_decode_h6144(h6144_experts):
-    _sampled_parity("decode_h6144", h6144_experts, n_sample=32)
+    _h6144_parity("decode_h6144", h6144_experts)
 
 
 def test_prefill_h6144(h6144_experts):
-    _sampled_parity("prefill_h6144", h6144_experts)
+    _h6144_parity("prefill_h6144", h6144_experts)
 
 
 def test_skewed_h6144(h6144_experts):
-    _sampled_parity("skewed_h6144", h6144_experts)
+    _h6144_parity("skewed_h6144", h6144_experts)
 
 
 def test_ep8_shard_h6144():
@@ -230,7 +238,7 @@ def test_ep8_shard_h6144():
     w = wl.WORKLOADS["ep8_shard_h6144"]
     experts = wl.expert_weights(w, device=DEV)
     try:
-        _sampled_parity("ep8_shard_h6144", experts, n_sample=24)
+        _h6144_parity("ep8_shard_h6144", experts)
     finally:
         del experts
         torch.cuda.empty_cache()
@@ -243,7 +251,7 @@ def test_inkling_default_h6144():
     _say("[parity] drawing the Inkling-default expert weights on the device (~29 GB)")
     experts = wl.expert_weights(w, device=DEV)
     try:
-        _sampled_parity("inkling_default_h6144", experts, n_sample=16)
+        _h6144_parity("inkling_default_h6144", experts)
     finally:
         del experts
         torch.cuda.empty_cache()
