@@ -73,15 +73,19 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(h))
 
 
-def run_timed(torch, B, call, steps, warmup, events: HipEvents, record=()):
+def run_timed(torch, B, call, steps, warmup, events: HipEvents, record=(), per_step=None):
     """Warmup, then `steps` timed calls.  `record` holds the stage boundaries
     (0..INKLING_STAGE_EVENTS-1) at which hipEvents are recorded on the library's
     stream during the timed calls ("all" = every boundary); an event record costs
     a few microseconds, so the headline run records only what it reports.
-    Returns (ms_per_step, {stage index: mean ms} for stages whose both
-    boundaries were recorded)."""
+    Returns (ms_per_step from the wall clock, {stage index: mean ms} for stages
+    whose both boundaries were recorded); `per_step`, if a list, receives each
+    step's duration in ms from events at the first and last boundaries
+    (inkling_moe_forward calls only: the other entry points record none)."""
     n_ev = B.INKLING_STAGE_EVENTS
     idx = set(range(n_ev)) if record == "all" else set(record)
+    if per_step is not None:
+        idx |= {0, n_ev - 1}
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -106,6 +110,8 @@ def run_timed(torch, B, call, steps, warmup, events: HipEvents, record=()):
     for s_i in range(1, n_ev):
         if s_i - 1 in idx and s_i in idx:
             stage[s_i - 1] = float(np.mean([events.elapsed_ms(ev[s_i - 1], ev[s_i]) for ev in sets]))
+    if per_step is not None:
+        per_step.extend(events.elapsed_ms(ev[0], ev[n_ev - 1]) for ev in sets)
     for ev in sets:
         events.destroy([h for h in ev if h])
     return (t1 - t0) * 1e3 / steps, stage
@@ -119,15 +125,17 @@ def gemm_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """Measured HBM bytes per gate_up launch, or None when the kernel source
-    changed since the counters were taken (or none were taken)."""
+def recorded_traffic(workload):
+    """Measured HBM bytes per gate_up launch on `workload`, or None when the
+    counters were taken on another workload, the kernel source changed since
+    they were taken, or none were taken."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m_h = re.search(r"^source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
     m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
-    if not m_h or not m_b or m_h.group(1) != gemm_source_hash():
+    m_w = re.search(r"^workload:\s*(\S+)\s*$", text, re.M)
+    if not m_h or not m_b or not m_w or m_h.group(1) != gemm_source_hash() or m_w.group(1) != workload:
         return None
     return float(m_b.group(1))
 
@@ -229,7 +237,8 @@ def main():
     events = HipEvents()
     gu = B.STAGES.index("gate_up")   # stage i lies between boundaries i and i+1
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
-    ms, st = run_timed(torch, B, call, args.steps, args.warmup, events, record=(gu, gu + 1))
+    step_ms = []
+    ms, st = run_timed(torch, B, call, args.steps, args.warmup, events, record=(gu, gu + 1), per_step=step_ms)
     _, st_all = run_timed(torch, B, call, args.steps, 2, events, record="all")
     flops = w.flops_alg()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -245,7 +254,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     roofline = {"kernel": "moe_gemm_kernel gate_up (routed + shared, SwiGLU epilogue)", "bound": "mfma",
                 "achieved": round(gu_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(gu_tflops / peak, 4), "traffic": recorded_traffic(),
+                "frac": round(gu_tflops / peak, 4), "traffic": recorded_traffic(w.name),
                 "per_launch": {"flops": gu_flops, "avg_ms": round(gu_ms, 4)}}
 
     result = {
@@ -256,6 +265,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        # each step's own duration from the hipEvents around it (value and
+        # ms_per_step come from the wall clock over all steps)
+        "ms_median": round(float(np.median(step_ms)), 4),
+        "ms_min": round(float(np.min(step_ms)), 4),
+        "ms_max": round(float(np.max(step_ms)), 4),
+        "TFLOP_s_at_median": round(flops / (float(np.median(step_ms)) * 1e-3) / 1e12, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -290,12 +305,15 @@ def main():
         dcall()
         torch.cuda.synchronize()
         n_touched = int((routing["expert_counts"] > 0).sum().item())
-        dms, _ = run_timed(torch, B, dcall, max(20, args.steps), args.warmup, events)
+        d_steps = []
+        dms, _ = run_timed(torch, B, dcall, max(20, args.steps), args.warmup, events, per_step=d_steps)
         _, dstage = run_timed(torch, B, dcall, max(20, args.steps), 2, events, record="all")
         eb = 2 if wd.dtype == "bf16" else 4
         bytes_alg = (3 * wd.hidden * wd.intermediate * eb * (n_touched + wd.n_shared)
                      + 4 * wd.hidden * (wd.n_routed + wd.n_shared) + 4 * wd.n_routed + 2 * eb * wd.T * wd.hidden)
         result["decode"] = {"workload": wd.name, "T": wd.T, "ms_per_step": round(dms, 4),
+                            "ms_median": round(float(np.median(d_steps)), 4),
+                            "ms_min": round(float(np.min(d_steps)), 4), "ms_max": round(float(np.max(d_steps)), 4),
                             "hbm_GBps": round(bytes_alg / (dms * 1e-3) / 1e9, 1),
                             "frac_of_peak": round(bytes_alg / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                             "bytes_alg": bytes_alg, "n_touched_experts": n_touched,
@@ -321,9 +339,13 @@ def main():
                 B.forward(oinp["x"], oinp["gate_bank"], oinp["bias"], oinp["w_gu"], oinp["w_d"], oinp["wsh_gu"],
                           oinp["wsh_d"], ow.top_k, ow.route_scale, ow.global_scale, out=oout, workspace=ows)
 
-            oms, _ = run_timed(torch, B, ocall, args.steps, args.warmup, events)
+            o_steps = []
+            oms, _ = run_timed(torch, B, ocall, args.steps, args.warmup, events, per_step=o_steps)
             otf = ow.flops_alg() / (oms * 1e-3) / 1e12
             result["other_workloads"][oname] = {"T": ow.T, "hidden": ow.hidden, "ms_per_step": round(oms, 4),
+                                                "ms_median": round(float(np.median(o_steps)), 4),
+                                                "ms_min": round(float(np.min(o_steps)), 4),
+                                                "ms_max": round(float(np.max(o_steps)), 4),
                                                 "TFLOP_s": round(otf, 2), "tokens_per_s": round(ow.T / (oms * 1e-3), 1),
                                                 "frac_of_peak": round(otf / PEAK_BF16_TFLOPS, 4)}
             log(f"[bench] {oname} {oms:.3f} ms, {otf:.1f} TFLOP/s")

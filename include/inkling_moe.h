@@ -137,7 +137,13 @@ int inkling_moe_route(const inkling_moe_dims_t* dims, const void* x, const inkli
 /* InklingMoE.forward: out[T][hidden] (dims->out_dtype) = sum over the selected
  * routed experts and all shared experts of gamma * expert(x).  out must not
  * alias x.  padding_mask as above (padded tokens get the shared experts only).
- * route_out may be NULL. */
+ * route_out may be NULL.
+ * Precision: products accumulate in fp32; the expert outputs are summed in
+ * fp32 in a fixed order and rounded once, so the result is bit-reproducible.
+ * With dtype INKLING_BF16 the activation between an expert's two projections,
+ * gamma * silu(gate) * up, is rounded to fp16 (nearest even), and the bf16
+ * down weights are taken as fp16, which is exact for 2^-17 <= |w| < 2^16;
+ * the activation must stay below 65504 in magnitude (above it is inf). */
 int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
                         const inkling_experts_t* experts, const uint8_t* padding_mask, void* out,
                         inkling_route_out_t* route_out, void* workspace, size_t workspace_bytes,
@@ -230,7 +236,8 @@ int inkling_dense_mlp_forward(const inkling_dense_dims_t* dims, const void* x, c
  * events[0] before the first launch and events[i] after stage i:
  *   1 router logits, 2 router selection, 3 permutation (masks, scan, scatter),
  *   4 gate_up grouped GEMM + SwiGLU (routed and shared),
- *   5 down grouped GEMM (routed and shared), 6 combine.
+ *   5 routed down grouped GEMM, 6 shared down GEMM with the combine in its
+ *   epilogue (the combine alone when n_shared == 0).
  * events[] holds INKLING_STAGE_EVENTS hipEvent_t handles created by the caller
  * (a NULL entry skips that boundary); the array must stay valid until the hook
  * is cleared with NULL.  Adds no synchronisation.  Returns INKLING_ERR_INVALID_ARGUMENT if n_events is too

@@ -29,7 +29,7 @@ EXPORTED = ("inkling_moe_workspace_size", "inkling_moe_route", "inkling_moe_forw
             "inkling_moe_backward_workspace_size", "inkling_moe_backward", "inkling_moe_saved_size",
             "inkling_moe_forward_train")
 INKLING_STAGE_EVENTS = 7
-STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "combine")
+STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "shared_down_combine")
 
 
 class Dims(ctypes.Structure):

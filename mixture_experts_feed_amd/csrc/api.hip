@@ -24,7 +24,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
     int ksplit, W, cfg, bm, max_tiles;
     size_t zpart, topk_idx, topk_w, shared_g, masks, prefix, counts, offsets, tiles, num_tiles, round_counters;
-    size_t sorted_slots, row_token, row_gamma, pos, act_r, act_sh, y, ysh, total;
+    size_t sorted_slots, row_token, row_gamma, pos, act_r, act_sh, y, total;
 };
 
 int check_dims(const inkling_moe_dims_t* d) {
@@ -78,7 +78,6 @@ Layout make_layout(const inkling_moe_dims_t* d) {
     L.act_r = take((size_t)T * k * I * es);
     L.act_sh = take((size_t)T * S * I * es);
     L.y = take((size_t)T * k * H * sizeof(float));
-    L.ysh = take((size_t)T * (S > 0 ? H : 0) * sizeof(float));
     L.total = o;
     return L;
 }
@@ -163,9 +162,9 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
 
 // ---- backward -----------------------------------------------------------------
 struct BwdLayout {
-    Layout F;   // the forward's routing and row buffers (y / ysh hold the dx rows)
+    Layout F;   // the forward's routing and row buffers (y holds the routed dx rows)
     int Tpad;
-    size_t h_r, h_sh, dh_r, dh_sh, dgp_r, dgp_sh, dz, dzc, poff, x_sorted, dout_sorted, zero, dbank_part, total;
+    size_t dx_sh, h_r, h_sh, dh_r, dh_sh, dgp_r, dgp_sh, dz, dzc, poff, x_sorted, dout_sorted, zero, dbank_part, total;
 };
 
 BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
@@ -186,6 +185,7 @@ BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
         o = align_up(o + bytes);
         return at;
     };
+    B.dx_sh = take(T * (S > 0 ? H : 0) * 4);
     B.h_r = take(T * k * 2 * I * 4);
     B.h_sh = take(T * S * 2 * I * 4);
     B.dh_r = take(T * k * 2 * I * es);
@@ -215,7 +215,7 @@ int check_dense_dims(const inkling_dense_dims_t* d) {
 }
 
 struct DenseLayout {
-    size_t gamma, round_counters, act, ysh, total;
+    size_t gamma, round_counters, act, total;
 };
 
 DenseLayout make_dense_layout(const inkling_dense_dims_t* d) {
@@ -230,7 +230,6 @@ DenseLayout make_dense_layout(const inkling_dense_dims_t* d) {
     L.gamma = take(T * 4);
     L.round_counters = take(kRoundCounters * 4);
     L.act = take(T * (size_t)d->intermediate * es);
-    L.ysh = take(T * (size_t)d->hidden * 4);
     L.total = o;
     return L;
 }
@@ -345,7 +344,6 @@ int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_ga
     p.act_r = at<void>(workspace, L.act_r);
     p.act_sh = at<void>(workspace, L.act_sh);
     p.y = at<void>(workspace, L.y);
-    p.ysh = at<void>(workspace, L.ysh);
     p.out = out;
     p.max_routed_tiles = L.max_tiles;
     p.round_counters = at<int32_t>(workspace, L.round_counters);
@@ -358,7 +356,8 @@ int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_ga
     HIP_TRY(mark(4, s));
     HIP_TRY(launch_down(p, s));
     HIP_TRY(mark(5, s));
-    HIP_TRY(launch_combine(p, s));
+    if (dims->n_shared > 0) HIP_TRY(launch_down_out(p, s));
+    else HIP_TRY(launch_combine(p, s));
     HIP_TRY(mark(6, s));
     return INKLING_OK;
 }
@@ -426,14 +425,12 @@ int inkling_dense_mlp_forward(const inkling_dense_dims_t* dims, const void* x, c
     p.wsh_d = down;
     p.shared_g = at<float>(workspace, L.gamma);
     p.act_sh = at<void>(workspace, L.act);
-    p.ysh = at<void>(workspace, L.ysh);
     p.out = out;
     p.round_counters = at<int32_t>(workspace, L.round_counters);
     p.has_routed = 0;
     HIP_TRY(launch_dense_prep(at<float>(workspace, L.gamma), T, global_scale, p.round_counters, s));
     HIP_TRY(launch_gate_up(p, s));
-    HIP_TRY(launch_down(p, s));
-    HIP_TRY(launch_combine(p, s));
+    HIP_TRY(launch_down_out(p, s));
     return INKLING_OK;
 }
 
@@ -555,8 +552,8 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
 
     // 5. dx rows: the gate_up projections against dh (the down-GEMM shape,
     //    K = 2I); then dx = shared + routed rows + gate term, rounded once
-    HIP_TRY(launch_dx(p, ab.dh_r, ab.dh_sh, at<void>(workspace, L.y), at<void>(workspace, L.ysh), s));
-    HIP_TRY(launch_dx_combine(p.out_dtype, at<float>(workspace, L.y), S > 0 ? at<float>(workspace, L.ysh) : nullptr,
+    HIP_TRY(launch_dx(p, ab.dh_r, ab.dh_sh, at<void>(workspace, L.y), at<void>(workspace, B.dx_sh), s));
+    HIP_TRY(launch_dx_combine(p.out_dtype, at<float>(workspace, L.y), S > 0 ? at<float>(workspace, B.dx_sh) : nullptr,
                               rb.pos, rb.topk_idx, dzc, gate->gate_bank, dx, T, H, E, S, k, s));
 
     // 6. gate bank gradient

@@ -14,13 +14,16 @@
 //   gate_up  routed tiles (rows gathered through the expert-sorted token list,
 //            scaled by that slot's gamma) and shared tiles (all tokens against
 //            the S shared experts concatenated along N, scaled by the token's
-//            shared gamma) -> act_r, act_sh;
+//            shared gamma) -> act_r, act_sh (fp16 for bf16 layers, see ActOf);
 //   down     routed: act_r rows of each expert -> y, one fp32 row per routed
-//            slot t*k + i (rows of a token are adjacent); shared: act_sh
-//            [T][S*I] against the shared down weights concatenated along K, so
-//            the sum over shared experts happens inside the reduction -> ysh
-//            [T][H] fp32; one launch, shared tiles first;
-//   combine  out[t] = ysh[t] + sum_i y[t*k + i], rounded once.
+//            slot t*k + i (rows of a token are adjacent);
+//   down_out shared: act_sh [T][S*I] against the shared down weights
+//            concatenated along K, so the sum over shared experts happens
+//            inside the reduction; the epilogue adds the token's k routed y
+//            rows and rounds once: out[t] = shared + sum_i y[t*k + i].  (Two
+//            launches: a token's y rows come from tiles on every XCD, and the
+//            launch boundary is what makes them visible to the other XCDs' L2.)
+//   combine  only without shared experts: out[t] = sum_i y[t*k + i].
 // The backward reuses the same kernel with other epilogues and operands (see
 // the modes below and backward.hip).  Its products contract over the other
 // index of a stored matrix (the down weights over H, the gate_up weights over
@@ -46,8 +49,12 @@ namespace {
 //            partial sums of dact . silu(g) * u (the routing-weight gradient)
 // kModeWgrad: weight gradients, one problem per expert, K = that expert's rows
 // kModeDx: backward through gate_up: the down epilogue (fp32 rows)
+// kModeDownOut: the shared down projection with the combine in its epilogue:
+//            out[t] = (shared sum) + sum_i y[t*k + i], in fp32 in that order,
+//            rounded once to the output type (shared tiles only)
 // A is read as [K][N] in kModeDAct, kModeDx and kModeWgrad, B in kModeWgrad.
-enum { kModeGateUp = 0, kModeDown = 1, kModeGateUpRaw = 2, kModeDAct = 3, kModeWgrad = 4, kModeDx = 5 };
+enum { kModeGateUp = 0, kModeDown = 1, kModeGateUpRaw = 2, kModeDAct = 3, kModeWgrad = 4, kModeDx = 5,
+       kModeDownOut = 6 };
 template <int MODE>
 constexpr bool a_kn() { return MODE == kModeDAct || MODE == kModeDx || MODE == kModeWgrad; }
 template <int MODE>
@@ -89,7 +96,7 @@ struct GemmKArgs {
     const float* row_gamma;
     const float* shared_g;
     void* out_routed;          // gate_up: act_r [T*k][I] (sorted rows); down: y [T*k][H] fp32 (slot rows)
-    void* out_shared;          // gate_up: act_sh [T][S*I]; down: ysh [T][H] fp32
+    void* out_shared;          // gate_up: act_sh [T][S*I]; dx: the shared rows [T][H] fp32
     int T, H, I, S, k;
     int K_r, N_r, ntn_r;    // routed problem: K, N per expert, N tiles
     int K_s, N_s, ntn_s;    // shared problem
@@ -124,6 +131,13 @@ struct GemmKArgs {
     void* w_out_routed;        // [E][M][N], fp32 or (w_out_bf16) bf16
     void* w_out_shared;        // [S][M][N]
     int w_out_bf16;
+    // kModeDownOut: the routed rows of each token (fp32, slot rows t*k + i),
+    // slot -> sorted row (-1 for every slot of a padded token), the layer
+    // output [T][H] and its type (1: bf16)
+    const float* y_rows;
+    const int32_t* pos;
+    void* out_final;
+    int out_final_bf16;
 };
 
 template <typename TE>
@@ -457,7 +471,7 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
     // activation rows (written by gate_up, read by down): fp16 for bf16 layers,
     // so the bf16 down weights are converted to fp16 fragments (f16 MFMA)
     using TA = typename ActOf<TE>::type;
-    constexpr bool CVT = MODE == kModeDown && std::is_same<TE, bf16_t>::value;
+    constexpr bool CVT = (MODE == kModeDown || MODE == kModeDownOut) && std::is_same<TE, bf16_t>::value;
     constexpr int RBA = BN * (int)sizeof(TE), RBB = BM * (int)sizeof(TE);   // bytes per K row
     constexpr int CHA = RBA / 16, CHB = RBB / 16;                           // 16-byte chunks per K row
     constexpr int RPIA = 1024 / RBA, RPIB = 1024 / RBB;                     // K rows per wave load
@@ -830,6 +844,29 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
         }
     };
 
+    // kModeDownOut: out[t][n..n+3] = v + y[t*k + 0][n..] + ... + y[t*k + k-1][n..]
+    // (fp32, in that order, which is also the order of the combine kernel),
+    // rounded once.  A padded token has no routed rows (all its slots -1).
+    auto combine_store = [&](int t, int n, f32x4_t v) __attribute__((always_inline)) {
+        if constexpr (MODE == kModeDownOut) {
+            if (a.k > 0 && a.pos[(size_t)t * a.k] >= 0) {
+                const float* yr = a.y_rows + (size_t)t * a.k * a.H + n;
+                int i = 0;
+                for (; i + 4 <= a.k; i += 4) {
+                    f32x4_t u[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) u[q] = *reinterpret_cast<const f32x4_t*>(yr + (size_t)(i + q) * a.H);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v += u[q];
+                }
+                for (; i < a.k; ++i) v += *reinterpret_cast<const f32x4_t*>(yr + (size_t)i * a.H);
+            }
+            const float w[4] = {v[0], v[1], v[2], v[3]};
+            if (a.out_final_bf16) store4<bf16_t>(static_cast<bf16_t*>(a.out_final) + (size_t)t * a.H + n, w);
+            else store4<float>(static_cast<float*>(a.out_final) + (size_t)t * a.H + n, w);
+        }
+    };
+
     // NJ: 16-row token blocks computed (blocks past the last valid row skipped).
     //
     // Work of a stage = KS k-steps x 2 halves of the token blocks (half-steps).
@@ -1140,6 +1177,31 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                         float* hb = static_cast<float*>(cur.out) + (size_t)cur.t0 * cur.N + cur.n0 + wn0;
                         flush_f32(j, mb, [&](int r) -> float* { return hb + (size_t)(mb + r) * cur.N; });
                     }
+                } else if constexpr (MODE == kModeDownOut) {
+                    // the combine: each 16-byte chunk of a row (4 columns of one
+                    // token) gets the token's routed rows added in slot order
+                    // (8 lanes read 128 contiguous bytes of each y row), then is
+                    // rounded once and stored
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                        for (int i = 2 * hh; i < 2 * hh + 2; ++i)
+                            if (i < nvi)
+                                *reinterpret_cast<f32x4_t*>(ep + rw * kEpRowB + ((i - 2 * hh) * 16 + 4 * g4) * 4) =
+                                    acc[i][j];
+                        f32x4_t d[2];
+#pragma unroll
+                        for (int sgi = 0; sgi < 2; ++sgi) {
+                            const int c = ln + 64 * sgi, r = c >> 3, q = c & 7;
+                            d[sgi] = *reinterpret_cast<const f32x4_t*>(ep + r * kEpRowB + q * 16);
+                        }
+#pragma unroll
+                        for (int sgi = 0; sgi < 2; ++sgi) {
+                            const int c = ln + 64 * sgi, r = c >> 3, q = c & 7;
+                            if (mb + r < cur.rows_valid && 2 * hh + (q >> 2) < nvi)
+                                combine_store(cur.t0 + mb + r, cur.n0 + wn0 + 32 * hh + 4 * q, d[sgi]);
+                        }
+                    }
                 } else {
                     // fp32 rows: the layer output is rounded once, in the combine
                     float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) + cur.n0 + wn0;
@@ -1186,6 +1248,8 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                                 float w[4] = {v[0], v[1], v[2], v[3]};
                                 store4<float>(hs, w);
                             }
+                        } else if (MODE == kModeDownOut) {
+                            combine_store(cur.t0 + m, n, v);
                         } else {
                             // fp32 rows: the layer output is rounded once, in the combine
                             float w[4] = {v[0], v[1], v[2], v[3]};
@@ -1207,11 +1271,13 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
     }
 }
 
-// out[t][h] = ysh[t][h] (if S > 0) + sum over i < k of y[t*k + i][h] for the
-// slots that were dispatched (pos >= 0), in fp32, rounded once to TO.
+// out[t][h] = sum over i < k of y[t*k + i][h] for the slots that were
+// dispatched (pos >= 0), in fp32, rounded once to TO (the layer without shared
+// experts; with them, the combine runs in the shared down projection's
+// epilogue).
 // One thread per 4 consecutive columns of one token; H % 4 == 0.
 template <typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ pos, TO* __restrict__ out, int T,
                                                       int H, int k) {
     const int hq = H >> 2;
@@ -1220,7 +1286,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
          idx += (size_t)gridDim.x * blockDim.x) {
         const int t = (int)(idx / hq);
         const int c = (int)(idx - (size_t)t * hq) * 4;
-        float4 s = ysh ? *reinterpret_cast<const float4*>(ysh + (size_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
         const int32_t* pt = pos + (size_t)t * k;
         const float* yt = y + (size_t)t * k * H + c;
 #pragma unroll 4
@@ -1270,7 +1336,7 @@ constexpr int kPrefillGM = 8;
 template <int MODE>
 constexpr int prefill_sched() {
     return MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kSchedRound
-           : MODE == kModeDown || MODE == kModeDx                            ? kSchedGroup
+           : MODE == kModeDown || MODE == kModeDx || MODE == kModeDownOut    ? kSchedGroup
                                                                               : kSchedQueue;
 }
 constexpr int kSyncMinRounds = 8;
@@ -1385,40 +1451,53 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
+    if (!p.has_routed) return hipSuccess;
     GemmKArgs a = base_args(p);
-    const int bm = gemm_cfg_bm(p.cfg);
     a.A_routed = p.w_d;
     a.B_routed = p.act_r;
     a.out_routed = p.y;
     a.K_r = p.I;
     a.N_r = p.H;
     a.ntn_r = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
-    a.has_routed = p.has_routed;
-    // shared experts: act_sh [T][S*I] against the S down projections concatenated along K
+    a.has_routed = 1;
+    a.shared_blocks = 0;
+    a.round_counter = p.round_counters + 8;
+    return launch_dispatch<kModeDown>(p, a, p.max_routed_tiles * a.ntn_r, stream);
+}
+
+hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream) {
+    GemmKArgs a = base_args(p);
+    const int bm = gemm_cfg_bm(p.cfg);
+    // act_sh [T][S*I] against the S down projections concatenated along K (the
+    // sum over shared experts happens inside the reduction), then the routed
+    // rows added in the epilogue
     a.A_shared = p.wsh_d;
     a.B_shared = p.act_sh;
-    a.out_shared = p.ysh;
     a.K_s = p.S * p.I;
     a.N_s = p.H;
-    a.ntn_s = a.ntn_r;
+    a.ntn_s = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
     a.seg_s = p.I;
     a.shared_mtiles = (p.T + bm - 1) / bm;
-    a.shared_blocks = p.S > 0 ? a.shared_mtiles * a.ntn_s : 0;
-    a.round_counter = p.round_counters + 8;
-    return launch_dispatch<kModeDown>(p, a, a.shared_blocks + (p.has_routed ? p.max_routed_tiles * a.ntn_r : 0),
-                                      stream);
+    a.shared_blocks = a.shared_mtiles * a.ntn_s;
+    a.has_routed = 0;
+    a.round_counter = p.round_counters + 16;
+    a.y_rows = p.has_routed ? static_cast<const float*>(p.y) : nullptr;
+    a.pos = p.pos;
+    a.k = p.has_routed ? p.k : 0;
+    a.out_final = p.out;
+    a.out_final_bf16 = p.out_dtype == 1 ? 1 : 0;
+    return launch_dispatch<kModeDownOut>(p, a, a.shared_blocks, stream);
 }
 
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream) {
     const size_t items = (size_t)p.T * (p.H / 4);
     const int blocks = (int)std::min<size_t>((items + 255) / 256, (size_t)num_cus() * 16);
-    const float* ysh = p.S > 0 ? reinterpret_cast<const float*>(p.ysh) : nullptr;
     const float* y = reinterpret_cast<const float*>(p.y);
     if (p.out_dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
+        hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, y, p.pos,
                            reinterpret_cast<bf16_t*>(p.out), p.T, p.H, p.k);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, p.pos,
                            reinterpret_cast<float*>(p.out), p.T, p.H, p.k);
     return hipGetLastError();
 }

@@ -65,7 +65,6 @@ struct MoeGemmParams {
     void* act_r;   // [T*k][I] sorted rows
     void* act_sh;  // [T][S*I]
     void* y;       // [T*k][H] fp32, slot rows
-    void* ysh;     // [T][H] fp32
     void* out;     // [T][H]
     float* h_save_r;   // optional: gate_up projection of the routed rows [T*k][2I] fp32 (sorted rows)
     float* h_save_sh;  // optional: ... of the shared experts [T][S*2I] fp32
@@ -78,8 +77,13 @@ struct MoeGemmParams {
 int gemm_cfg_for(int T, int E, int k);
 int gemm_cfg_bm(int cfg);
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
-// routed (act_r -> y) and shared (act_sh -> ysh) down projections, one launch
+// routed down projection: act_r rows -> y (fp32, one row per slot t*k + i)
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream);
+// shared down projection (act_sh against the S down weights concatenated along
+// K) with the combine in its epilogue: out[t] = shared sum + sum_i y[t*k + i],
+// rounded once (S > 0; without routed rows, has_routed = 0, just the shared sum)
+hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream);
+// out[t] = sum_i y[t*k + i] rounded once: the combine of a layer without shared experts
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream);
 // ---- backward GEMMs (gemm.hip) ---------------------------------------------
 // h = gate_up(x) (no SwiGLU, fp32) for routed rows [T*k][2I] and shared [T][S*2I]

@@ -23,6 +23,14 @@ import oracle
 TIE_BAND = 1e-12
 GAMMA_RTOL = 1e-5
 OUT_TOL = {"bf16": 2e-2, "f32": 1e-4}
+# bf16 weight gradients: each element is a sum over rows of products u_r v_r
+# of which one factor is rounded to bf16 (unit roundoff 2^-8) and the other is
+# an exact input, accumulated in fp32 (K 2^-24 <= 2^-10 for K <= 16384 rows):
+# |err| <= (2^-8 + 2^-10) sum_r |u_r v_r|
+WGRAD_ABS_BOUND = 2.0 ** -8 + 2.0 ** -10
+# weight-gradient K stages hold 32 rows of K (64-byte bf16 rows); K is an
+# expert's row count padded to a multiple of 64
+WGRAD_STAGE_ROWS = 32
 
 
 class HostExperts:
@@ -95,3 +103,37 @@ def check_output(out_gpu, out_ref, dtype, rows=None):
     err = float(np.max(np.abs(g - out_ref))) if out_ref.size else 0.0
     assert err <= OUT_TOL[dtype] * rms, f"max abs err {err:.3e} > {OUT_TOL[dtype]} * RMS {rms:.3e}"
     return err / rms if rms > 0 else 0.0
+
+
+def wgrad_excess(g, ref, absref):
+    """Elements of a bf16 weight gradient g above the componentwise bound
+    WGRAD_ABS_BOUND * sum|u v| (plus 1e-6 RMS for the fp32 error already in
+    the rounded factor).  Returns (number above, worst |err| / sum|u v|)."""
+    g = np.asarray(g, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    absref = np.asarray(absref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    diff = np.abs(g - ref)
+    excess = diff - WGRAD_ABS_BOUND * absref - 1e-6 * rms
+    worst = float(np.max(diff / (absref + 1e-30 * rms + 1e-300))) if ref.size else 0.0
+    return int(np.sum(excess > 0)), worst
+
+
+def stage_edge_rows(n_rows, stage=WGRAD_STAGE_ROWS, extra=()):
+    """Row positions of a weight-gradient K loop where a dropped, doubled or
+    misplaced row is most likely: the first and last row of every eighth
+    stage, the rows around the start of the middle stage, and rows spread over
+    the last stage, which holds the padding when n_rows is not a multiple of
+    64 (rows n_rows .. the next multiple read zeros).  About 30 rows for a few
+    thousand."""
+    rows = set()
+    n_st = (n_rows + stage - 1) // stage
+    for st in range(0, n_st, max(1, n_st // 8)):
+        rows.update((st * stage, st * stage + stage - 1))
+    mid = (n_st // 2) * stage
+    rows.update((mid - 1, mid, mid + 1))
+    last0 = ((n_rows - 1) // stage) * stage
+    rows.update(range(last0, n_rows, max(1, (n_rows - last0) // 6)))
+    rows.update((n_rows - 2, n_rows - 1))
+    rows.update(extra)
+    return sorted(r for r in rows if 0 <= r < n_rows)

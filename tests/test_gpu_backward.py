@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 TOL = {"bf16": 2e-2, "f32": 1e-4}
-ABS_BOUND = 2.0 ** -8 + 2.0 ** -10
+ABS_BOUND = P.WGRAD_ABS_BOUND
 
 
 def _say(msg):
@@ -57,13 +57,11 @@ def _close_wgrad(name, gpu, ref, absref, dtype):
     if dtype == "f32":
         return _close(name, gpu, ref, dtype)
     g = gpu.float().cpu().numpy().astype(np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    rms = float(np.sqrt(np.mean(ref ** 2)))
-    excess = np.abs(g - ref) - ABS_BOUND * np.asarray(absref) - 1e-6 * rms
-    worst = float(np.max(np.abs(g - ref) / (np.asarray(absref) + 1e-30 * rms + 1e-300)))
+    n_above, worst = P.wgrad_excess(g, ref, absref)
+    rms = float(np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2)))
     _say(f"[backward]   {name}: max |err| / sum|u v| = {worst:.2e} (bound {ABS_BOUND:.2e}), "
          f"max_err/rms={float(np.max(np.abs(g - ref))) / rms if rms > 0 else 0.0:.2e}")
-    assert np.all(excess <= 0), f"{name}: {int(np.sum(excess > 0))} elements above the bound"
+    assert n_above == 0, f"{name}: {n_above} elements above the bound"
     return worst
 
 
@@ -76,10 +74,13 @@ def _run(w, inp, dout, padding_mask=None):
     return out
 
 
-def _full_backward(w, padding_mask=None):
+def _full_backward(w, padding_mask=None, dout=None, dout_rows=None):
+    """dout_rows: the only tokens where dout is non-zero; dx is then compared
+    on those rows (its RMS over all rows would be diluted by exact zeros), and
+    must be exactly zero on the others."""
     _say(f"[backward] {w}")
     inp = wl.make_inputs(w, device=DEV)
-    dout = _dout(w)
+    dout = _dout(w) if dout is None else dout
     g = _run(w, inp, dout, padding_mask)
     S = w.n_shared
     pm = None if padding_mask is None else padding_mask.cpu().numpy().astype(bool)
@@ -89,10 +90,16 @@ def _full_backward(w, padding_mask=None):
                               w.top_k, w.route_scale, w.global_scale, P.host(dout), padding_mask=pm, with_abs=True)
     E = w.n_routed
     st = lambda d: np.stack([d[e] for e in range(E)])
-    rel = {"dx": _close("dx", g["dx"], ref["dx"], w.dtype),
+    if dout_rows is not None:
+        others = np.setdiff1d(np.arange(w.T), dout_rows)
+        assert not bool(g["dx"][torch.as_tensor(others, device=g["dx"].device)].any()), "dx non-zero where dout is 0"
+        rel = {"dx": _close("dx", g["dx"][list(dout_rows)], ref["dx"][dout_rows], w.dtype)}
+    else:
+        rel = {"dx": _close("dx", g["dx"], ref["dx"], w.dtype)}
+    rel.update({
            "d_gate_bank": _close("d_gate_bank", g["d_gate_bank"], ref["d_gate_bank"], w.dtype),
            "d_w_gu": _close_wgrad("d_w_gu", g["d_w_gu"], st(ref["d_w_gu"]), st(ref["abs_w_gu"]), w.dtype),
-           "d_w_d": _close_wgrad("d_w_d", g["d_w_d"], st(ref["d_w_d"]), st(ref["abs_w_d"]), w.dtype)}
+           "d_w_d": _close_wgrad("d_w_d", g["d_w_d"], st(ref["d_w_d"]), st(ref["abs_w_d"]), w.dtype)})
     if S:
         rel["d_wsh_gu"] = _close_wgrad("d_wsh_gu", g["d_wsh_gu"], ref["d_wsh_gu"], ref["abs_wsh_gu"], w.dtype)
         rel["d_wsh_d"] = _close_wgrad("d_wsh_d", g["d_wsh_d"], ref["d_wsh_d"], ref["abs_wsh_d"], w.dtype)
@@ -135,6 +142,26 @@ def test_backward_every_token_padded(S):
     assert not bool(g["d_w_gu"].any()) and not bool(g["d_w_d"].any())
     if S == 0:
         assert not bool(g["dx"].any()) and not bool(g["d_gate_bank"].any())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_sparse_dout_at_stage_edges(dtype):
+    """Experts of 4083 rows (every token picks all four experts, so row r of
+    each expert is token r; K pads to 4096) with dout non-zero only on about
+    30 tokens: the first and last rows of K stages, the rows around a middle
+    stage start, and rows of the padded last stage.  Each weight-gradient
+    element then sums over those rows only, so the componentwise bf16 bound
+    (and the fp32 RMS bar) sees any dropped, doubled or misplaced row of the
+    K loop; tests/test_parity_bars.py shows the bound rejecting such errors."""
+    w = wl.custom(name=f"sparse_dout_{dtype}", T=4083, hidden=256, n_routed=4, top_k=4, n_shared=1,
+                  intermediate=128, dtype=dtype, route_scale=2.5, gate_dist=("uniform", 0.05),
+                  bias_dist=("uniform", 0.05))
+    rows = P.stage_edge_rows(w.T)
+    g = torch.Generator().manual_seed(13)
+    dout = torch.zeros((w.T, w.hidden), dtype=torch.float32)
+    dout[rows] = torch.randn((len(rows), w.hidden), generator=g)
+    _say(f"[backward] sparse dout on {len(rows)} rows: {rows}")
+    _full_backward(w, dout=dout.to(w.torch_dtype).to(DEV), dout_rows=rows)
 
 
 def test_backward_small_bf16():

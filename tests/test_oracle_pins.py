@@ -84,6 +84,22 @@ def test_topk_zero_bias_is_topk_of_logits():
     assert np.array_equal(idx, ref)
 
 
+def test_topk_margin_hand_set():
+    """s_(k) - s_(k+1): the k-th largest score minus the (k+1)-th, per row.
+    Scores with distinct gaps (1/8, 1/4, 3/8, 1/2 in descending order) give
+    a different margin for every k, so an off-by-one in either index fails;
+    k = E has nothing left out (inf); an exact tie at the cut gives 0."""
+    s = np.array([[0.125, 0.875, -0.375, 0.5, 0.75]])   # descending: .875 .75 .5 .125 -.375
+    want = {1: 0.125, 2: 0.25, 3: 0.375, 4: 0.5}
+    for k, m in want.items():
+        assert oracle.topk_margin(s, k)[0] == m, k
+    assert np.isinf(oracle.topk_margin(s, 5)[0])
+    ties = np.array([[0.5, 0.25, 0.5, -1.0], [0.25, 0.5, 0.75, 1.0]])
+    assert oracle.topk_margin(ties, 1).tolist() == [0.0, 0.25]
+    assert oracle.topk_margin(ties, 2).tolist() == [0.25, 0.25]
+    assert oracle.topk_margin(ties, 3).tolist() == [1.25, 0.25]
+
+
 def test_bias_changes_selection_not_weights():
     """The correction bias steers selection only; the weights come from the
     unbiased logits (InklingGate: selection uses sigmoid + bias, weights use the
