@@ -77,7 +77,7 @@ Layout make_layout(const inkling_moe_dims_t* d) {
     L.pos = take((size_t)T * k * 4);
     L.act_r = take((size_t)T * k * I * es);
     L.act_sh = take((size_t)T * S * I * es);
-    L.y = take((size_t)T * k * H * sizeof(float));
+    L.y = take((size_t)T * k * H * es);   // fp16 rows for bf16 layers, fp32 for fp32 ones
     L.total = o;
     return L;
 }
@@ -162,9 +162,9 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
 
 // ---- backward -----------------------------------------------------------------
 struct BwdLayout {
-    Layout F;   // the forward's routing and row buffers (y holds the routed dx rows)
+    Layout F;   // the forward's routing and row buffers
     int Tpad;
-    size_t dx_sh, h_r, h_sh, dh_r, dh_sh, dgp_r, dgp_sh, dz, dzc, poff, x_sorted, dout_sorted, zero, dbank_part, total;
+    size_t dx_r, dx_sh, h_r, h_sh, dh_r, dh_sh, dgp_r, dgp_sh, dz, dzc, poff, x_sorted, dout_sorted, zero, dbank_part, total;
 };
 
 BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
@@ -185,6 +185,7 @@ BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
         o = align_up(o + bytes);
         return at;
     };
+    B.dx_r = take(T * k * H * 4);
     B.dx_sh = take(T * (S > 0 ? H : 0) * 4);
     B.h_r = take(T * k * 2 * I * 4);
     B.h_sh = take(T * S * 2 * I * 4);
@@ -552,8 +553,8 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
 
     // 5. dx rows: the gate_up projections against dh (the down-GEMM shape,
     //    K = 2I); then dx = shared + routed rows + gate term, rounded once
-    HIP_TRY(launch_dx(p, ab.dh_r, ab.dh_sh, at<void>(workspace, L.y), at<void>(workspace, B.dx_sh), s));
-    HIP_TRY(launch_dx_combine(p.out_dtype, at<float>(workspace, L.y), S > 0 ? at<float>(workspace, B.dx_sh) : nullptr,
+    HIP_TRY(launch_dx(p, ab.dh_r, ab.dh_sh, at<void>(workspace, B.dx_r), at<void>(workspace, B.dx_sh), s));
+    HIP_TRY(launch_dx_combine(p.out_dtype, at<float>(workspace, B.dx_r), S > 0 ? at<float>(workspace, B.dx_sh) : nullptr,
                               rb.pos, rb.topk_idx, dzc, gate->gate_bank, dx, T, H, E, S, k, s));
 
     // 6. gate bank gradient

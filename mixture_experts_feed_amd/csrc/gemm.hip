@@ -95,7 +95,7 @@ struct GemmKArgs {
     const int32_t* row_slot;   // sorted row -> slot t*k + i
     const float* row_gamma;
     const float* shared_g;
-    void* out_routed;          // gate_up: act_r [T*k][I] (sorted rows); down: y [T*k][H] fp32 (slot rows)
+    void* out_routed;          // gate_up: act_r [T*k][I] (sorted rows); down: y [T*k][H] (slot rows, TA)
     void* out_shared;          // gate_up: act_sh [T][S*I]; dx: the shared rows [T][H] fp32
     int T, H, I, S, k;
     int K_r, N_r, ntn_r;    // routed problem: K, N per expert, N tiles
@@ -131,10 +131,10 @@ struct GemmKArgs {
     void* w_out_routed;        // [E][M][N], fp32 or (w_out_bf16) bf16
     void* w_out_shared;        // [S][M][N]
     int w_out_bf16;
-    // kModeDownOut: the routed rows of each token (fp32, slot rows t*k + i),
-    // slot -> sorted row (-1 for every slot of a padded token), the layer
-    // output [T][H] and its type (1: bf16)
-    const float* y_rows;
+    // kModeDownOut: the routed rows of each token (slot rows t*k + i, fp16 for
+    // bf16 layers, fp32 for fp32 ones), slot -> sorted row (-1 for every slot
+    // of a padded token), the layer output [T][H] and its type (1: bf16)
+    const void* y_rows;
     const int32_t* pos;
     void* out_final;
     int out_final_bf16;
@@ -160,6 +160,10 @@ __device__ __forceinline__ void mma16<float>(f32x4_t& acc, const uint4& a, const
 // The activation between the two projections of a bf16 layer is kept in fp16,
 // not bf16: act = gamma silu(g) u is rounded once before the down projection,
 // and fp16's 11-bit significand makes that rounding 8x smaller than bf16's.
+// The routed experts' output rows y (summed per token by the combine) are
+// fp16 too, which halves their round trip through HBM; with fp16 act and fp16
+// y the skewed workload's error is about 5e-3 of the output RMS (bf16 y alone
+// would add about 3e-2).  Both must stay below 65504 in magnitude.
 // (On heavy-tailed inputs, where rows of 4x the norm give outputs far above the
 // RMS, the bf16 rounding alone reaches about 2.6e-2 of the output RMS; fp16
 // gives about 3e-3.)  The down weights stay bf16 in memory and are converted to
@@ -236,6 +240,25 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
 template <>
 __device__ __forceinline__ void store4<float>(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ void store4<f16_t>(f16_t* p, const float* v) {
+    const f16x2_t lo = {(f16_t)v[0], (f16_t)v[1]}, hi = {(f16_t)v[2], (f16_t)v[3]};   // nearest even
+    *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// four consecutive values widened to fp32
+template <typename TY>
+__device__ __forceinline__ f32x4_t load4f(const TY* p);
+template <>
+__device__ __forceinline__ f32x4_t load4f<float>(const float* p) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4_t load4f<f16_t>(const f16_t* p) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    const f16x2_t lo = __builtin_bit_cast(f16x2_t, q.x), hi = __builtin_bit_cast(f16x2_t, q.y);
+    return f32x4_t{(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
 }
 
 template <typename TE>
@@ -744,7 +767,8 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
 
     // per-row epilogue data, loaded when a tile starts (used after its K loop)
     float ep_g0[FM], ep_g1[FM];   // gate_up: gamma of the row (routed) / of the wave's first and last shared expert
-    int ep_row[FM];               // down: output row (slot for routed tiles, token for shared tiles)
+    int ep_row[FM];               // down: output row (slot for routed tiles, token for shared tiles);
+                                  // down_out: 1 if the row's token has routed rows
     int ep_s0 = 0;                // gate_up shared: expert of the wave's first weight row
     auto prefetch_epilogue = [&](const Tile<TE>& t) __attribute__((always_inline)) {
         if constexpr (MODE == kModeGateUpRaw || MODE == kModeWgrad) return;
@@ -764,6 +788,8 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                     ep_g0[j] = a.row_gamma[t.grow0 + m];
                     ep_g1[j] = 0.f;
                 }
+            } else if (MODE == kModeDownOut) {
+                ep_row[j] = a.k > 0 && a.pos[(size_t)(t.t0 + m) * a.k] >= 0;   // the token has routed rows
             } else {
                 ep_row[j] = t.is_shared ? t.t0 + m : a.row_slot[t.grow0 + m];
             }
@@ -846,20 +872,23 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
 
     // kModeDownOut: out[t][n..n+3] = v + y[t*k + 0][n..] + ... + y[t*k + k-1][n..]
     // (fp32, in that order, which is also the order of the combine kernel),
-    // rounded once.  A padded token has no routed rows (all its slots -1).
-    auto combine_store = [&](int t, int n, f32x4_t v) __attribute__((always_inline)) {
+    // rounded once.  `routed`: the token was dispatched (a padded token has no
+    // routed rows), read with the other per-row epilogue data.
+    auto combine_store = [&](int t, int n, f32x4_t v, int routed) __attribute__((always_inline)) {
         if constexpr (MODE == kModeDownOut) {
-            if (a.k > 0 && a.pos[(size_t)t * a.k] >= 0) {
-                const float* yr = a.y_rows + (size_t)t * a.k * a.H + n;
-                int i = 0;
-                for (; i + 4 <= a.k; i += 4) {
-                    f32x4_t u[4];
+            if (routed) {
+                // the first 8 rows are loaded unconditionally (a smaller k
+                // re-reads its last row, not added), so all 8 are in flight
+                // before the first add; then the rest one by one
+                const TA* yr = static_cast<const TA*>(a.y_rows) + (size_t)t * a.k * a.H + n;
+                const int k8 = min(a.k, 8);
+                f32x4_t u[8];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) u[q] = *reinterpret_cast<const f32x4_t*>(yr + (size_t)(i + q) * a.H);
+                for (int q = 0; q < 8; ++q) u[q] = load4f<TA>(yr + (size_t)min(q, k8 - 1) * a.H);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v += u[q];
-                }
-                for (; i < a.k; ++i) v += *reinterpret_cast<const f32x4_t*>(yr + (size_t)i * a.H);
+                for (int q = 0; q < 8; ++q)
+                    if (q < k8) v += u[q];
+                for (int i = 8; i < a.k; ++i) v += load4f<TA>(yr + (size_t)i * a.H);
             }
             const float w[4] = {v[0], v[1], v[2], v[3]};
             if (a.out_final_bf16) store4<bf16_t>(static_cast<bf16_t*>(a.out_final) + (size_t)t * a.H + n, w);
@@ -1195,15 +1224,36 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             const int c = ln + 64 * sgi, r = c >> 3, q = c & 7;
                             d[sgi] = *reinterpret_cast<const f32x4_t*>(ep + r * kEpRowB + q * 16);
                         }
+                        const int er = ep_row[j];
 #pragma unroll
                         for (int sgi = 0; sgi < 2; ++sgi) {
                             const int c = ln + 64 * sgi, r = c >> 3, q = c & 7;
+                            const int routed = __shfl(er, r);
                             if (mb + r < cur.rows_valid && 2 * hh + (q >> 2) < nvi)
-                                combine_store(cur.t0 + mb + r, cur.n0 + wn0 + 32 * hh + 4 * q, d[sgi]);
+                                combine_store(cur.t0 + mb + r, cur.n0 + wn0 + 32 * hh + 4 * q, d[sgi], routed);
                         }
                     }
+                } else if constexpr (MODE == kModeDown && sizeof(TA) == 2) {
+                    // routed rows rounded to fp16: the wave's 64 columns of 16
+                    // rows pass through LDS as 128-byte row segments
+#pragma unroll
+                    for (int i = 0; i < FN; ++i)
+                        if (i < nvi) {
+                            const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                            store4<TA>(reinterpret_cast<TA*>(ep + rw * kEpRowB + (16 * i + 4 * g4) * 2), v4);
+                        }
+                    TA* o = reinterpret_cast<TA*>(a.out_routed) + cur.n0 + wn0;
+                    const int er = ep_row[j];
+#pragma unroll
+                    for (int sgi = 0; sgi < 2; ++sgi) {
+                        const int c = ln + 64 * sgi, r = c >> 3, q = c & 7;
+                        const uint4 d = *reinterpret_cast<const uint4*>(ep + r * kEpRowB + q * 16);
+                        const int row = __shfl(er, r);
+                        if (mb + r < cur.rows_valid && (q >> 1) < nvi)
+                            *reinterpret_cast<uint4*>(o + (size_t)row * a.H + 8 * q) = d;
+                    }
                 } else {
-                    // fp32 rows: the layer output is rounded once, in the combine
+                    // fp32 rows (the routed rows of fp32 layers; dx rows)
                     float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) + cur.n0 + wn0;
                     const int er = ep_row[j];
                     flush_f32(j, mb, [&](int r) -> float* { return o + (size_t)__shfl(er, r) * a.H; });
@@ -1249,9 +1299,13 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                                 store4<float>(hs, w);
                             }
                         } else if (MODE == kModeDownOut) {
-                            combine_store(cur.t0 + m, n, v);
+                            combine_store(cur.t0 + m, n, v, ep_row[j]);
+                        } else if (MODE == kModeDown) {
+                            // routed rows (TA: fp16 for bf16 layers)
+                            float w[4] = {v[0], v[1], v[2], v[3]};
+                            store4<TA>(reinterpret_cast<TA*>(a.out_routed) + (size_t)ep_row[j] * a.H + n, w);
                         } else {
-                            // fp32 rows: the layer output is rounded once, in the combine
+                            // fp32 rows (dx)
                             float w[4] = {v[0], v[1], v[2], v[3]};
                             float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed);
                             store4<float>(o + (size_t)ep_row[j] * a.H + n, w);
@@ -1276,8 +1330,8 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
 // experts; with them, the combine runs in the shared down projection's
 // epilogue).
 // One thread per 4 consecutive columns of one token; H % 4 == 0.
-template <typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+template <typename TY, typename TO>
+__global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y,
                                                       const int32_t* __restrict__ pos, TO* __restrict__ out, int T,
                                                       int H, int k) {
     const int hq = H >> 2;
@@ -1288,15 +1342,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         const int c = (int)(idx - (size_t)t * hq) * 4;
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
         const int32_t* pt = pos + (size_t)t * k;
-        const float* yt = y + (size_t)t * k * H + c;
+        const TY* yt = y + (size_t)t * k * H + c;
 #pragma unroll 4
         for (int i = 0; i < k; ++i) {
             if (pt[i] >= 0) {
-                const float4 v = *reinterpret_cast<const float4*>(yt + (size_t)i * H);
-                s.x += v.x;
-                s.y += v.y;
-                s.z += v.z;
-                s.w += v.w;
+                const f32x4_t v = load4f<TY>(yt + (size_t)i * H);
+                s.x += v[0];
+                s.y += v[1];
+                s.z += v[2];
+                s.w += v[3];
             }
         }
         float w[4] = {s.x, s.y, s.z, s.w};
@@ -1481,7 +1535,7 @@ hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream) {
     a.shared_blocks = a.shared_mtiles * a.ntn_s;
     a.has_routed = 0;
     a.round_counter = p.round_counters + 16;
-    a.y_rows = p.has_routed ? static_cast<const float*>(p.y) : nullptr;
+    a.y_rows = p.has_routed ? p.y : nullptr;
     a.pos = p.pos;
     a.k = p.has_routed ? p.k : 0;
     a.out_final = p.out;
@@ -1489,16 +1543,22 @@ hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream) {
     return launch_dispatch<kModeDownOut>(p, a, a.shared_blocks, stream);
 }
 
+template <typename TY>
+void combine_typed(const MoeGemmParams& p, int blocks, hipStream_t stream) {
+    const TY* y = reinterpret_cast<const TY*>(p.y);
+    if (p.out_dtype == 1)
+        hipLaunchKernelGGL((combine_kernel<TY, bf16_t>), dim3(blocks), dim3(256), 0, stream, y, p.pos,
+                           reinterpret_cast<bf16_t*>(p.out), p.T, p.H, p.k);
+    else
+        hipLaunchKernelGGL((combine_kernel<TY, float>), dim3(blocks), dim3(256), 0, stream, y, p.pos,
+                           reinterpret_cast<float*>(p.out), p.T, p.H, p.k);
+}
+
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream) {
     const size_t items = (size_t)p.T * (p.H / 4);
     const int blocks = (int)std::min<size_t>((items + 255) / 256, (size_t)num_cus() * 16);
-    const float* y = reinterpret_cast<const float*>(p.y);
-    if (p.out_dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, stream, y, p.pos,
-                           reinterpret_cast<bf16_t*>(p.out), p.T, p.H, p.k);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, p.pos,
-                           reinterpret_cast<float*>(p.out), p.T, p.H, p.k);
+    if (p.dtype == 1) combine_typed<f16_t>(p, blocks, stream);   // the routed rows of bf16 layers are fp16
+    else combine_typed<float>(p, blocks, stream);
     return hipGetLastError();
 }
 

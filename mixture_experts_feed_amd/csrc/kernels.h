@@ -64,7 +64,7 @@ struct MoeGemmParams {
     const int32_t* pos;         // slot -> sorted row, -1 if not dispatched
     void* act_r;   // [T*k][I] sorted rows
     void* act_sh;  // [T][S*I]
-    void* y;       // [T*k][H] fp32, slot rows
+    void* y;       // [T*k][H] slot rows: fp16 for bf16 layers, fp32 for fp32 ones
     void* out;     // [T][H]
     float* h_save_r;   // optional: gate_up projection of the routed rows [T*k][2I] fp32 (sorted rows)
     float* h_save_sh;  // optional: ... of the shared experts [T][S*2I] fp32
@@ -77,7 +77,8 @@ struct MoeGemmParams {
 int gemm_cfg_for(int T, int E, int k);
 int gemm_cfg_bm(int cfg);
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
-// routed down projection: act_r rows -> y (fp32, one row per slot t*k + i)
+// routed down projection: act_r rows -> y (one row per slot t*k + i; fp16 for
+// bf16 layers, fp32 for fp32 ones)
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream);
 // shared down projection (act_sh against the S down weights concatenated along
 // K) with the combine in its epilogue: out[t] = shared sum + sum_i y[t*k + i],
