@@ -36,9 +36,11 @@
  *       shared_down    [n_shared][hidden][I]
  *   - The caller flattens leading dimensions of the hidden states to T rows.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- *     and is asynchronous.  The library never allocates device memory, never
- *     frees, never synchronises.  Scratch lives in the caller's workspace.
- *     Calls that share a workspace must be ordered on one stream.
+ *     and is asynchronous.  No call allocates or frees device memory or
+ *     synchronises.  Scratch lives in the caller's workspace, except for
+ *     inkling_moe_forward_noalloc, whose scratch is a static device array that
+ *     comes with the library's code on each GPU.  Calls that share a workspace
+ *     must be ordered on one stream.
  *   - Arguments are checked on the host before anything is launched; an error
  *     return means nothing was enqueued (except INKLING_ERR_HIP, which reports
  *     a failed launch).
@@ -63,6 +65,7 @@ extern "C" {
 #define INKLING_ERR_UNSUPPORTED (-2)      /* dtype or size outside the limits above */
 #define INKLING_ERR_WORKSPACE (-3)        /* workspace NULL or smaller than inkling_moe_workspace_size() */
 #define INKLING_ERR_HIP (-4)              /* a HIP launch failed; see inkling_moe_last_hip_error() */
+#define INKLING_ERR_TOO_LARGE (-5)        /* sizes need more scratch than inkling_moe_forward_noalloc holds */
 
 typedef enum { INKLING_F32 = 0, INKLING_BF16 = 1 } inkling_dtype_t;
 
@@ -148,6 +151,26 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
                         const inkling_experts_t* experts, const uint8_t* padding_mask, void* out,
                         inkling_route_out_t* route_out, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * inkling_moe_forward without the workspace argument, bit for bit the same
+ * results.  Its scratch is a static device array of
+ * INKLING_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held from the
+ * library's load on that GPU until the process ends; the call allocates and
+ * frees nothing.  Returns INKLING_ERR_TOO_LARGE, before anything is enqueued,
+ * when inkling_moe_workspace_size() for these dims exceeds that size (at
+ * hidden 6144, top-8, 2 shared experts, intermediate 2048 that is above 429
+ * tokens; decode batches of 32 tokens need 5 MB).  Every call on one GPU uses that GPU's one array, and the
+ * array keeps what the last call left there: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be ordered on one
+ * stream.  The device is the calling thread's current HIP device.
+ */
+#define INKLING_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int inkling_moe_forward_noalloc(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                                const inkling_experts_t* experts, const uint8_t* padding_mask, void* out,
+                                inkling_route_out_t* route_out, void* stream);
 
 /*
  * Training forward: inkling_moe_forward (same out, bit for bit) that also

@@ -20,6 +20,8 @@ INKLING_ERR_INVALID_ARGUMENT = -1
 INKLING_ERR_UNSUPPORTED = -2
 INKLING_ERR_WORKSPACE = -3
 INKLING_ERR_HIP = -4
+INKLING_ERR_TOO_LARGE = -5
+INKLING_NOALLOC_SCRATCH_BYTES = 64 << 20
 INKLING_F32 = 0
 INKLING_BF16 = 1
 
@@ -27,7 +29,7 @@ EXPORTED = ("inkling_moe_workspace_size", "inkling_moe_route", "inkling_moe_forw
             "inkling_moe_strerror", "inkling_moe_last_hip_error", "inkling_moe_set_stage_events",
             "inkling_dense_mlp_workspace_size", "inkling_dense_mlp_forward",
             "inkling_moe_backward_workspace_size", "inkling_moe_backward", "inkling_moe_saved_size",
-            "inkling_moe_forward_train")
+            "inkling_moe_forward_train", "inkling_moe_forward_noalloc")
 INKLING_STAGE_EVENTS = 7
 STAGES = ("router_logits", "router_select", "permutation", "gate_up", "down", "shared_down_combine")
 
@@ -95,6 +97,10 @@ def load() -> ctypes.CDLL:
                                         ctypes.POINTER(Experts), ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.POINTER(RouteOut), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.inkling_moe_forward.restype = ctypes.c_int
+    lib.inkling_moe_forward_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.POINTER(Gate),
+                                                ctypes.POINTER(Experts), ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.POINTER(RouteOut), ctypes.c_void_p]
+    lib.inkling_moe_forward_noalloc.restype = ctypes.c_int
     lib.inkling_moe_strerror.argtypes = [ctypes.c_int]
     lib.inkling_moe_strerror.restype = ctypes.c_char_p
     lib.inkling_moe_last_hip_error.argtypes = []
@@ -203,15 +209,9 @@ def route(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, top_k: i
     return res
 
 
-def forward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: torch.Tensor, w_d: torch.Tensor,
-            wsh_gu: Optional[torch.Tensor], wsh_d: Optional[torch.Tensor], top_k: int, route_scale: float,
-            global_scale: float, padding_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
-            out_dtype: Optional[torch.dtype] = None, saved: Optional[torch.Tensor] = None):
-    """inkling_moe_forward: out [T, H] (x's dtype unless out / out_dtype says
-    otherwise) and the routing dict if asked.  With `saved` (uint8, saved_size
-    bytes) it is inkling_moe_forward_train, which also keeps the gate_up
-    projections there for backward()."""
+def _forward_args(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k, route_scale, global_scale, padding_mask,
+                  out, return_routing, out_dtype):
+    """Checks and C structs shared by forward() and forward_noalloc()."""
     T, H = x.shape
     E, twoI, _ = w_gu.shape
     S = 0 if wsh_gu is None else wsh_gu.shape[0]
@@ -235,7 +235,7 @@ def forward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: 
     if padding_mask is not None:
         _need(padding_mask, "padding_mask", torch.uint8)
     routing = None
-    ro_ptr = None
+    ro = None
     if return_routing:
         routing = {
             "topk_indices": torch.empty((T, top_k), dtype=torch.int32, device=dev),
@@ -247,9 +247,24 @@ def forward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: 
         }
         ro = RouteOut(*[_ptr(routing[n]) for n in ("topk_indices", "topk_weights", "shared_gammas",
                                                    "expert_counts", "expert_offsets", "sorted_slots")])
-        ro_ptr = ctypes.byref(ro)
     gate = Gate(gate_bank.data_ptr(), bias.data_ptr(), float(route_scale), float(global_scale))
     ex = Experts(w_gu.data_ptr(), w_d.data_ptr(), _ptr(wsh_gu) if S else None, _ptr(wsh_d) if S else None)
+    return dims, gate, ex, out, routing, ro
+
+
+def forward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: torch.Tensor, w_d: torch.Tensor,
+            wsh_gu: Optional[torch.Tensor], wsh_d: Optional[torch.Tensor], top_k: int, route_scale: float,
+            global_scale: float, padding_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
+            out_dtype: Optional[torch.dtype] = None, saved: Optional[torch.Tensor] = None):
+    """inkling_moe_forward: out [T, H] (x's dtype unless out / out_dtype says
+    otherwise) and the routing dict if asked.  With `saved` (uint8, saved_size
+    bytes) it is inkling_moe_forward_train, which also keeps the gate_up
+    projections there for backward()."""
+    dims, gate, ex, out, routing, ro = _forward_args(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k,
+                                                     route_scale, global_scale, padding_mask, out, return_routing,
+                                                     out_dtype)
+    dev = x.device
     if workspace is None:
         workspace = alloc_workspace(dims, dev)
     if saved is not None:
@@ -264,10 +279,29 @@ def forward(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: 
             raise InklingError(rc, "inkling_moe_forward_train")
         return out
     rc = load().inkling_moe_forward(ctypes.byref(dims), x.data_ptr(), ctypes.byref(gate), ctypes.byref(ex),
-                                    _ptr(padding_mask), out.data_ptr(), ro_ptr, workspace.data_ptr(),
-                                    workspace.numel(), _stream(dev))
+                                    _ptr(padding_mask), out.data_ptr(), None if ro is None else ctypes.byref(ro),
+                                    workspace.data_ptr(), workspace.numel(), _stream(dev))
     if rc != INKLING_OK:
         raise InklingError(rc, "inkling_moe_forward")
+    return (out, routing) if return_routing else out
+
+
+def forward_noalloc(x: torch.Tensor, gate_bank: torch.Tensor, bias: torch.Tensor, w_gu: torch.Tensor,
+                    w_d: torch.Tensor, wsh_gu: Optional[torch.Tensor], wsh_d: Optional[torch.Tensor], top_k: int,
+                    route_scale: float, global_scale: float, padding_mask: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, return_routing: bool = False,
+                    out_dtype: Optional[torch.dtype] = None):
+    """inkling_moe_forward_noalloc: forward() without a workspace (the
+    library's static scratch of INKLING_NOALLOC_SCRATCH_BYTES per GPU).  With
+    `out` given and no routing asked for, this allocates nothing."""
+    dims, gate, ex, out, routing, ro = _forward_args(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k,
+                                                     route_scale, global_scale, padding_mask, out, return_routing,
+                                                     out_dtype)
+    rc = load().inkling_moe_forward_noalloc(ctypes.byref(dims), x.data_ptr(), ctypes.byref(gate), ctypes.byref(ex),
+                                            _ptr(padding_mask), out.data_ptr(),
+                                            None if ro is None else ctypes.byref(ro), _stream(x.device))
+    if rc != INKLING_OK:
+        raise InklingError(rc, "inkling_moe_forward_noalloc")
     return (out, routing) if return_routing else out
 
 

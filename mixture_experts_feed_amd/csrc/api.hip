@@ -2,6 +2,9 @@
 // layout and the launch sequence (router -> permutation -> grouped GEMMs).
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/inkling_moe.h"
 #include "common.h"
 #include "kernels.h"
@@ -374,6 +377,60 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
     return forward_impl(dims, x, gate, w, padding_mask, out, r, nullptr, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// ---- the forward with a static scratch (no workspace argument) ----------------
+namespace {
+
+// One array per GPU, in the library's device code: each device it runs on
+// holds its own copy from the module's load until the process ends.  In host
+// code the name `scratch` is a host-side stand-in, not a device address; the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is ever passed on.
+__device__ __align__(256) uint8_t scratch[INKLING_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return INKLING_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return INKLING_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int inkling_moe_forward_noalloc(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
+                                const inkling_experts_t* w, const uint8_t* padding_mask, void* out,
+                                inkling_route_out_t* r, void* stream) {
+    const int rc = check_dims(dims);
+    if (rc != INKLING_OK) return rc;
+    if (dims->T == 0) return INKLING_OK;
+    // every buffer the forward reads is written by it first (its counters are
+    // zeroed by the permutation), so what an earlier call left does not matter
+    if (make_layout(dims).total > INKLING_NOALLOC_SCRATCH_BYTES) return INKLING_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    const int rs = scratch_of_current_device(&ws);
+    if (rs != INKLING_OK) return rs;
+    return forward_impl(dims, x, gate, w, padding_mask, out, r, nullptr, ws, INKLING_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int inkling_moe_saved_size(const inkling_moe_dims_t* dims, size_t* bytes) {
     const int rc = check_dims(dims);
     if (rc != INKLING_OK) return rc;
@@ -622,6 +679,9 @@ const char* inkling_moe_strerror(int code) {
         case INKLING_ERR_UNSUPPORTED: return "unsupported dtype or size";
         case INKLING_ERR_WORKSPACE: return "workspace missing or too small";
         case INKLING_ERR_HIP: return "HIP launch failed (see inkling_moe_last_hip_error)";
+        case INKLING_ERR_TOO_LARGE:
+            return "sizes need more scratch than the static array of inkling_moe_forward_noalloc "
+                   "(INKLING_NOALLOC_SCRATCH_BYTES); use inkling_moe_forward with a workspace";
         default: return "unknown error code";
     }
 }

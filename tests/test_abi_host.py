@@ -135,7 +135,7 @@ def test_zero_tokens_is_a_noop(lib):
 
 
 def test_strerror(lib):
-    for c in (0, -1, -2, -3, -4, -99):
+    for c in (0, -1, -2, -3, -4, -5, -99):
         assert isinstance(lib.inkling_moe_strerror(c), bytes)
     assert lib.inkling_moe_last_hip_error() == 0
 
@@ -239,3 +239,35 @@ def test_largest_token_count_accepted(lib):
     assert rc == B.INKLING_OK and n > 0
     rc, _ = _ws(lib, T=2 ** 31 - 256, top_k=1)
     assert rc == B.INKLING_ERR_UNSUPPORTED
+
+
+def _noalloc(lib, d):
+    gate = B.Gate(None, None, 1.0, 1.0)
+    return lib.inkling_moe_forward_noalloc(ctypes.byref(d), None, ctypes.byref(gate), None, None, None, None, None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+INKLING_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.INKLING_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """inkling_moe_forward_noalloc returns INKLING_ERR_TOO_LARGE, before any
+    HIP call, exactly when the workspace of the same dims exceeds its static
+    scratch (the first token count past the limit at the prefill shapes);
+    bad dims give the usual codes and T = 0 is a no-op."""
+    shape = dict(hidden=6144, n_routed=128, top_k=8, n_shared=2, intermediate=2048)
+    cap = B.INKLING_NOALLOC_SCRATCH_BYTES
+    lo, hi = 1, 1 << 16
+    while lo < hi:   # largest T whose workspace fits
+        mid = (lo + hi + 1) // 2
+        rc, n = _ws(lib, T=mid, **shape)
+        assert rc == B.INKLING_OK
+        lo, hi = (mid, hi) if n <= cap else (lo, mid - 1)
+    assert 32 < lo < 8192   # decode batches fit, prefill batches do not
+    assert _noalloc(lib, _dims(T=lo + 1, **shape)) == B.INKLING_ERR_TOO_LARGE
+    assert _noalloc(lib, _dims(T=8192, **shape)) == B.INKLING_ERR_TOO_LARGE
+    assert _noalloc(lib, _dims(T=-1)) == B.INKLING_ERR_INVALID_ARGUMENT
+    assert _noalloc(lib, _dims(hidden=96)) == B.INKLING_ERR_UNSUPPORTED
+    assert _noalloc(lib, _dims(T=0)) == B.INKLING_OK
