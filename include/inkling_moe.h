@@ -260,7 +260,9 @@ int inkling_dense_mlp_forward(const inkling_dense_dims_t* dims, const void* x, c
  *   1 router logits, 2 router selection, 3 permutation (masks, scan, scatter),
  *   4 gate_up grouped GEMM + SwiGLU (routed and shared),
  *   5 routed down grouped GEMM, 6 shared down GEMM with the combine in its
- *   epilogue (the combine alone when n_shared == 0).
+ *   epilogue.  (With few tokens per expert, at most 48 on average, the shared
+ *   down tiles run in stage 5 and stage 6 is the combine alone, as it is when
+ *   n_shared == 0.)
  * events[] holds INKLING_STAGE_EVENTS hipEvent_t handles created by the caller
  * (a NULL entry skips that boundary); the array must stay valid until the hook
  * is cleared with NULL.  Adds no synchronisation.  Returns INKLING_ERR_INVALID_ARGUMENT if n_events is too

@@ -1233,7 +1233,7 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                                 combine_store(cur.t0 + mb + r, cur.n0 + wn0 + 32 * hh + 4 * q, d[sgi], routed);
                         }
                     }
-                } else if constexpr (MODE == kModeDown && sizeof(TA) == 2) {
+                } else if (MODE == kModeDown && sizeof(TA) == 2 && !cur.is_shared) {
                     // routed rows rounded to fp16: the wave's 64 columns of 16
                     // rows pass through LDS as 128-byte row segments
 #pragma unroll
@@ -1253,7 +1253,8 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             *reinterpret_cast<uint4*>(o + (size_t)row * a.H + 8 * q) = d;
                     }
                 } else {
-                    // fp32 rows (the routed rows of fp32 layers; dx rows)
+                    // fp32 rows (the routed rows of fp32 layers; the shared sums
+                    // of a down launch; dx rows)
                     float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) + cur.n0 + wn0;
                     const int er = ep_row[j];
                     flush_f32(j, mb, [&](int r) -> float* { return o + (size_t)__shfl(er, r) * a.H; });
@@ -1300,12 +1301,12 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             }
                         } else if (MODE == kModeDownOut) {
                             combine_store(cur.t0 + m, n, v, ep_row[j]);
-                        } else if (MODE == kModeDown) {
+                        } else if (MODE == kModeDown && !cur.is_shared) {
                             // routed rows (TA: fp16 for bf16 layers)
                             float w[4] = {v[0], v[1], v[2], v[3]};
                             store4<TA>(reinterpret_cast<TA*>(a.out_routed) + (size_t)ep_row[j] * a.H + n, w);
                         } else {
-                            // fp32 rows (dx)
+                            // fp32 rows (the shared sums of a down launch; dx)
                             float w[4] = {v[0], v[1], v[2], v[3]};
                             float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed);
                             store4<float>(o + (size_t)ep_row[j] * a.H + n, w);
@@ -1325,13 +1326,14 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
     }
 }
 
-// out[t][h] = sum over i < k of y[t*k + i][h] for the slots that were
-// dispatched (pos >= 0), in fp32, rounded once to TO (the layer without shared
-// experts; with them, the combine runs in the shared down projection's
-// epilogue).
+// out[t][h] = ysh[t][h] (if given) + sum over i < k of y[t*k + i][h] for the
+// slots that were dispatched (pos >= 0), in fp32 in that order, rounded once
+// to TO: the combine of a layer without shared experts, and of the few-token
+// tiles, whose down launch also computes the shared sums ysh (with the
+// 256 x 256 tiles the combine runs in the shared down projection's epilogue).
 // One thread per 4 consecutive columns of one token; H % 4 == 0.
 template <typename TY, typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, const float* __restrict__ ysh,
                                                       const int32_t* __restrict__ pos, TO* __restrict__ out, int T,
                                                       int H, int k) {
     const int hq = H >> 2;
@@ -1340,7 +1342,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y,
          idx += (size_t)gridDim.x * blockDim.x) {
         const int t = (int)(idx / hq);
         const int c = (int)(idx - (size_t)t * hq) * 4;
-        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 s = ysh ? *reinterpret_cast<const float4*>(ysh + (size_t)t * H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
         const int32_t* pt = pos + (size_t)t * k;
         const TY* yt = y + (size_t)t * k * H + c;
 #pragma unroll 4
@@ -1386,11 +1388,15 @@ constexpr int kPrefillGM = 8;
 //   rounds);
 // - short-K tiles (down, dx, weight gradients): the queue (down 1-3%, the
 //   backward 3% faster than the plain stride; the rendezvous was slower);
-//   for down and dx the partner-group start (another 1.2-1.4% on down).
+//   for dx and the shared down + combine the partner-group start (which gave
+//   down another 1.2-1.4% while it converted no operand; with the fp16
+//   weight fragments and fp16 rows the queue is 1.2% faster for the routed
+//   down: 1.79-1.80 ms against 1.82; the shared down + combine runs at the
+//   same speed under every order, 0.59-0.60 ms).
 template <int MODE>
 constexpr int prefill_sched() {
     return MODE == kModeGateUp || MODE == kModeGateUpRaw || MODE == kModeDAct ? kSchedRound
-           : MODE == kModeDown || MODE == kModeDx || MODE == kModeDownOut    ? kSchedGroup
+           : MODE == kModeDx || MODE == kModeDownOut                          ? kSchedGroup
                                                                               : kSchedQueue;
 }
 constexpr int kSyncMinRounds = 8;
@@ -1505,7 +1511,6 @@ hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
-    if (!p.has_routed) return hipSuccess;
     GemmKArgs a = base_args(p);
     a.A_routed = p.w_d;
     a.B_routed = p.act_r;
@@ -1513,10 +1518,26 @@ hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
     a.K_r = p.I;
     a.N_r = p.H;
     a.ntn_r = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
-    a.has_routed = 1;
+    a.has_routed = p.has_routed;
     a.shared_blocks = 0;
+    if (p.cfg != 0 && p.S > 0) {
+        // few-token tiles: the shared experts' tiles join this launch (act_sh
+        // [T][S*I] against the S down projections concatenated along K, fp32
+        // sums to ysh), so that their weights stream with the routed ones;
+        // the combine kernel then adds ysh and the routed rows
+        a.A_shared = p.wsh_d;
+        a.B_shared = p.act_sh;
+        a.out_shared = p.ysh;
+        a.K_s = p.S * p.I;
+        a.N_s = p.H;
+        a.ntn_s = a.ntn_r;
+        a.seg_s = p.I;
+        a.shared_mtiles = (p.T + gemm_cfg_bm(p.cfg) - 1) / gemm_cfg_bm(p.cfg);
+        a.shared_blocks = a.shared_mtiles * a.ntn_s;
+    }
     a.round_counter = p.round_counters + 8;
-    return launch_dispatch<kModeDown>(p, a, p.max_routed_tiles * a.ntn_r, stream);
+    return launch_dispatch<kModeDown>(p, a, a.shared_blocks + (p.has_routed ? p.max_routed_tiles * a.ntn_r : 0),
+                                      stream);
 }
 
 hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream) {
@@ -1546,11 +1567,12 @@ hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream) {
 template <typename TY>
 void combine_typed(const MoeGemmParams& p, int blocks, hipStream_t stream) {
     const TY* y = reinterpret_cast<const TY*>(p.y);
+    const float* ysh = p.S > 0 ? static_cast<const float*>(p.ysh) : nullptr;
     if (p.out_dtype == 1)
-        hipLaunchKernelGGL((combine_kernel<TY, bf16_t>), dim3(blocks), dim3(256), 0, stream, y, p.pos,
+        hipLaunchKernelGGL((combine_kernel<TY, bf16_t>), dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
                            reinterpret_cast<bf16_t*>(p.out), p.T, p.H, p.k);
     else
-        hipLaunchKernelGGL((combine_kernel<TY, float>), dim3(blocks), dim3(256), 0, stream, y, p.pos,
+        hipLaunchKernelGGL((combine_kernel<TY, float>), dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
                            reinterpret_cast<float*>(p.out), p.T, p.H, p.k);
 }
 
