@@ -26,6 +26,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     int ksplit, W, cfg, bm, max_tiles;
+    bool fused;
     size_t zpart, topk_idx, topk_w, shared_g, masks, prefix, counts, offsets, tiles, num_tiles, round_counters;
     size_t sorted_slots, row_token, row_gamma, pos, act_r, act_sh, y, ysh, total;
 };
@@ -81,9 +82,10 @@ Layout make_layout(const inkling_moe_dims_t* d) {
     L.act_r = take((size_t)T * k * I * es);
     L.act_sh = take((size_t)T * S * I * es);
     L.y = take((size_t)T * k * H * es);   // fp16 rows for bf16 layers, fp32 for fp32 ones
-    // fp32 shared sums: the few-token tiles only (the 256 x 256 tiles add the
-    // routed rows in the shared down projection's epilogue)
-    L.ysh = take(L.cfg != 0 && S > 0 ? (size_t)T * H * sizeof(float) : 0);
+    // fp32 shared sums, unless the routed rows are added in the shared down
+    // projection's epilogue
+    L.fused = gemm_fused_combine(L.cfg, (int)T, H, S);
+    L.ysh = take(S > 0 && !L.fused ? (size_t)T * H * sizeof(float) : 0);
     L.total = o;
     return L;
 }
@@ -352,6 +354,7 @@ int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_ga
     p.act_sh = at<void>(workspace, L.act_sh);
     p.y = at<void>(workspace, L.y);
     p.ysh = at<void>(workspace, L.ysh);
+    p.fused_combine = L.fused ? 1 : 0;
     p.out = out;
     p.max_routed_tiles = L.max_tiles;
     p.round_counters = at<int32_t>(workspace, L.round_counters);
@@ -364,7 +367,7 @@ int forward_impl(const inkling_moe_dims_t* dims, const void* x, const inkling_ga
     HIP_TRY(mark(4, s));
     HIP_TRY(launch_down(p, s));
     HIP_TRY(mark(5, s));
-    if (dims->n_shared > 0 && L.cfg == 0) HIP_TRY(launch_down_out(p, s));
+    if (L.fused) HIP_TRY(launch_down_out(p, s));
     else HIP_TRY(launch_combine(p, s));
     HIP_TRY(mark(6, s));
     return INKLING_OK;

@@ -1328,9 +1328,9 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
 
 // out[t][h] = ysh[t][h] (if given) + sum over i < k of y[t*k + i][h] for the
 // slots that were dispatched (pos >= 0), in fp32 in that order, rounded once
-// to TO: the combine of a layer without shared experts, and of the few-token
-// tiles, whose down launch also computes the shared sums ysh (with the
-// 256 x 256 tiles the combine runs in the shared down projection's epilogue).
+// to TO: the combine of a layer without shared experts, and of launches whose
+// down launch also computes the shared sums ysh (otherwise the combine runs in
+// the shared down projection's epilogue; see gemm_fused_combine).
 // One thread per 4 consecutive columns of one token; H % 4 == 0.
 template <typename TY, typename TO>
 __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, const float* __restrict__ ysh,
@@ -1485,6 +1485,17 @@ int gemm_cfg_for(int T, int E, int k) {
 
 int gemm_cfg_bm(int cfg) { return cfg == 0 ? 256 : 16; }
 
+// Fused only with a full round of shared tiles on the 256 CUs: below that the
+// shared launch leaves CUs idle (the small workload's 128 tiles: 78 us for the
+// shared down and combine), while its tiles cost little inside the routed
+// launch.  A fixed count, so that the workspace size needs no device query.
+constexpr int kFuseMinSharedTiles = 256;
+bool gemm_fused_combine(int cfg, int T, int H, int S) {
+    if (cfg != 0 || S <= 0) return false;
+    const long long tiles = (long long)((T + 255) / 256) * ((H + kPrefillBN - 1) / kPrefillBN);
+    return tiles >= kFuseMinSharedTiles;
+}
+
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream) {
     GemmKArgs a = base_args(p);
     const int bm = gemm_cfg_bm(p.cfg);
@@ -1520,11 +1531,12 @@ hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream) {
     a.ntn_r = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);
     a.has_routed = p.has_routed;
     a.shared_blocks = 0;
-    if (p.cfg != 0 && p.S > 0) {
-        // few-token tiles: the shared experts' tiles join this launch (act_sh
-        // [T][S*I] against the S down projections concatenated along K, fp32
-        // sums to ysh), so that their weights stream with the routed ones;
-        // the combine kernel then adds ysh and the routed rows
+    if (p.S > 0 && !p.fused_combine) {
+        // the shared experts' tiles join this launch (act_sh [T][S*I] against
+        // the S down projections concatenated along K, fp32 sums to ysh), so
+        // that they fill the routed launch's rounds (and, with few-token
+        // tiles, their weights stream with the routed ones); the combine
+        // kernel then adds ysh and the routed rows
         a.A_shared = p.wsh_d;
         a.B_shared = p.act_sh;
         a.out_shared = p.ysh;
@@ -1567,7 +1579,7 @@ hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream) {
 template <typename TY>
 void combine_typed(const MoeGemmParams& p, int blocks, hipStream_t stream) {
     const TY* y = reinterpret_cast<const TY*>(p.y);
-    const float* ysh = p.S > 0 ? static_cast<const float*>(p.ysh) : nullptr;
+    const float* ysh = p.S > 0 && p.has_routed ? static_cast<const float*>(p.ysh) : nullptr;
     if (p.out_dtype == 1)
         hipLaunchKernelGGL((combine_kernel<TY, bf16_t>), dim3(blocks), dim3(256), 0, stream, y, ysh, p.pos,
                            reinterpret_cast<bf16_t*>(p.out), p.T, p.H, p.k);

@@ -65,7 +65,8 @@ struct MoeGemmParams {
     void* act_r;   // [T*k][I] sorted rows
     void* act_sh;  // [T][S*I]
     void* y;       // [T*k][H] slot rows: fp16 for bf16 layers, fp32 for fp32 ones
-    void* ysh;     // [T][H] fp32 shared sums (few-token tiles only; see launch_down)
+    void* ysh;     // [T][H] fp32 shared sums (when the combine is not fused; see launch_down)
+    int fused_combine;   // gemm_fused_combine(cfg, T, H, S)
     void* out;     // [T][H]
     float* h_save_r;   // optional: gate_up projection of the routed rows [T*k][2I] fp32 (sorted rows)
     float* h_save_sh;  // optional: ... of the shared experts [T][S*2I] fp32
@@ -77,17 +78,22 @@ struct MoeGemmParams {
 // average, then 1 (128 weight rows x 16 tokens)
 int gemm_cfg_for(int T, int E, int k);
 int gemm_cfg_bm(int cfg);
+// whether the combine runs in the epilogue of a shared down launch of its own
+// (256 x 256 tiles and at least one round of shared tiles, 256 or more), or the
+// shared down tiles join the routed down launch (fp32 sums ysh) and the combine
+// kernel follows
+bool gemm_fused_combine(int cfg, int T, int H, int S);
 hipError_t launch_gate_up(const MoeGemmParams& p, hipStream_t stream);
 // routed down projection: act_r rows -> y (one row per slot t*k + i; fp16 for
-// bf16 layers, fp32 for fp32 ones); with the few-token tiles (cfg 1) and
-// shared experts, the shared down projection in the same launch -> ysh (fp32)
+// bf16 layers, fp32 for fp32 ones); with shared experts and no fused combine,
+// the shared down projection in the same launch -> ysh (fp32)
 hipError_t launch_down(const MoeGemmParams& p, hipStream_t stream);
 // shared down projection (act_sh against the S down weights concatenated along
 // K) with the combine in its epilogue: out[t] = shared sum + sum_i y[t*k + i],
 // rounded once (S > 0; without routed rows, has_routed = 0, just the shared sum)
 hipError_t launch_down_out(const MoeGemmParams& p, hipStream_t stream);
-// out[t] = ysh[t] (cfg 1 with shared experts) + sum_i y[t*k + i], rounded
-// once: the combine of the few-token tiles and of a layer without shared experts
+// out[t] = ysh[t] (shared experts) + sum_i y[t*k + i], rounded once: the
+// combine when it is not fused, and of a layer without shared experts
 hipError_t launch_combine(const MoeGemmParams& p, hipStream_t stream);
 // ---- backward GEMMs (gemm.hip) ---------------------------------------------
 // h = gate_up(x) (no SwiGLU, fp32) for routed rows [T*k][2I] and shared [T][S*2I]
