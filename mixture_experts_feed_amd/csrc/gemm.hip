@@ -978,12 +978,30 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             // its first half-step, after the wait above)
                             if constexpr (half == 0) {
 #pragma unroll
-                                for (int i = 0; i < FN; ++i) fa[acur][i] = bf16x8_to_f16x8(fa[acur][i]);
+                                for (int i = 0; i < FN; ++i) {
+                                    fa[acur][i] = bf16x8_to_f16x8(fa[acur][i]);
+#pragma unroll
+                                    for (int j = 0; j < jn; ++j)
+                                        mma16_f16(acc[i][jbase + j], fa[acur][i], fb[bcur][j]);
+                                }
+                                // the 12 VALU ops converting fragment i + 1 issue
+                                // between the MFMAs of fragment i, which do not
+                                // wait for them
+                                constexpr int cv = 12 / jn;
+                                __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+#pragma unroll
+                                for (int g = 0; g < (FN - 1) * jn; ++g) {
+                                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                                    __builtin_amdgcn_sched_group_barrier(0x002, cv, 0);
+                                }
+                                __builtin_amdgcn_sched_group_barrier(0x008, jn, 0);
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                                    for (int j = 0; j < jn; ++j)
+                                        mma16_f16(acc[i][jbase + j], fa[acur][i], fb[bcur][j]);
                             }
-#pragma unroll
-                            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                                for (int j = 0; j < jn; ++j) mma16_f16(acc[i][jbase + j], fa[acur][i], fb[bcur][j]);
                         } else {
 #pragma unroll
                             for (int j = 0; j < jn; ++j)
