@@ -205,6 +205,9 @@ int inkling_moe_forward_train(const inkling_moe_dims_t* dims, const void* x, con
  * expert that receives no token gets zeros.
  *   dout [T][hidden] (dims->dtype);  dx [T][hidden] (dims->out_dtype), which
  *   must alias neither x nor dout.
+ * For bf16 layers each routed slot's share of dx is rounded to fp16 before
+ * the slots are summed in fp32 (like the forward's routed rows), so its
+ * elements must stay below 65504 in magnitude.
  * Weight gradients have the weights' layouts.  They are accumulated in fp32
  * and stored as fp32, or, with weight_grad_dtype = INKLING_BF16, rounded once
  * to nearest-even bf16 (half the bytes written; each value is the fp32

@@ -193,7 +193,7 @@ BwdLayout make_bwd_layout(const inkling_moe_dims_t* d) {
         o = align_up(o + bytes);
         return at;
     };
-    B.dx_r = take(T * k * H * 4);
+    B.dx_r = take(T * k * H * es);   // routed dx rows: fp16 for bf16 layers, else fp32
     B.dx_sh = take(T * (S > 0 ? H : 0) * 4);
     B.h_r = take(T * k * 2 * I * 4);
     B.h_sh = take(T * S * 2 * I * 4);
@@ -618,8 +618,9 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
     // 5. dx rows: the gate_up projections against dh (the down-GEMM shape,
     //    K = 2I); then dx = shared + routed rows + gate term, rounded once
     HIP_TRY(launch_dx(p, ab.dh_r, ab.dh_sh, at<void>(workspace, B.dx_r), at<void>(workspace, B.dx_sh), s));
-    HIP_TRY(launch_dx_combine(p.out_dtype, at<float>(workspace, B.dx_r), S > 0 ? at<float>(workspace, B.dx_sh) : nullptr,
-                              rb.pos, rb.topk_idx, dzc, gate->gate_bank, dx, T, H, E, S, k, s));
+    HIP_TRY(launch_dx_combine(dt, p.out_dtype, at<void>(workspace, B.dx_r),
+                              S > 0 ? at<float>(workspace, B.dx_sh) : nullptr, rb.pos, rb.topk_idx, dzc,
+                              gate->gate_bank, dx, T, H, E, S, k, s));
 
     // 6. gate bank gradient
     HIP_TRY(launch_dbank(dt, dz, x, T, H, E + S, at<float>(workspace, B.dbank_part), g->d_gate_bank, s));

@@ -1251,9 +1251,10 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                                 combine_store(cur.t0 + mb + r, cur.n0 + wn0 + 32 * hh + 4 * q, d[sgi], routed);
                         }
                     }
-                } else if (MODE == kModeDown && sizeof(TA) == 2 && !cur.is_shared) {
-                    // routed rows rounded to fp16: the wave's 64 columns of 16
-                    // rows pass through LDS as 128-byte row segments
+                } else if ((MODE == kModeDown || MODE == kModeDx) && sizeof(TA) == 2 && !cur.is_shared) {
+                    // routed rows (down: y, dx: the routed dx rows) rounded to
+                    // fp16: the wave's 64 columns of 16 rows pass through LDS as
+                    // 128-byte row segments
 #pragma unroll
                     for (int i = 0; i < FN; ++i)
                         if (i < nvi) {
@@ -1272,7 +1273,7 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                     }
                 } else {
                     // fp32 rows (the routed rows of fp32 layers; the shared sums
-                    // of a down launch; dx rows)
+                    // of a down launch and of dx)
                     float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed) + cur.n0 + wn0;
                     const int er = ep_row[j];
                     flush_f32(j, mb, [&](int r) -> float* { return o + (size_t)__shfl(er, r) * a.H; });
@@ -1319,12 +1320,12 @@ __global__ __launch_bounds__(WN * WM * 64, 512 / (WN * WM * 64)) void moe_gemm_k
                             }
                         } else if (MODE == kModeDownOut) {
                             combine_store(cur.t0 + m, n, v, ep_row[j]);
-                        } else if (MODE == kModeDown && !cur.is_shared) {
+                        } else if ((MODE == kModeDown || MODE == kModeDx) && !cur.is_shared) {
                             // routed rows (TA: fp16 for bf16 layers)
                             float w[4] = {v[0], v[1], v[2], v[3]};
                             store4<TA>(reinterpret_cast<TA*>(a.out_routed) + (size_t)ep_row[j] * a.H + n, w);
                         } else {
-                            // fp32 rows (the shared sums of a down launch; dx)
+                            // fp32 rows (the shared sums of a down launch and of dx)
                             float w[4] = {v[0], v[1], v[2], v[3]};
                             float* o = reinterpret_cast<float*>(cur.is_shared ? a.out_shared : a.out_routed);
                             store4<float>(o + (size_t)ep_row[j] * a.H + n, w);
@@ -1687,7 +1688,7 @@ hipError_t launch_dx(const MoeGemmParams& p, const void* dh_r, const void* dh_sh
     a.A_routed = p.w_gu;       // [E][2I][H]: K = 2I rows of H
     a.lda_r = p.H;
     a.B_routed = dh_r;         // [T*k][2I] sorted rows
-    a.out_routed = dx_r;       // [T*k][H] fp32, slot rows
+    a.out_routed = dx_r;       // [T*k][H] slot rows: fp16 for bf16 layers, else fp32
     a.K_r = 2 * p.I;
     a.N_r = p.H;
     a.ntn_r = (p.H + cfg_bn(p.cfg) - 1) / cfg_bn(p.cfg);

@@ -153,7 +153,10 @@ hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream);
 hipError_t launch_router_backward(const double* zpart, int ksplit, const int32_t* topk_idx, const int32_t* pos,
                                   const float* dgp_r, const float* dgp_sh, int T, int E, int S, int k, int I,
                                   float route_scale, float global_scale, float* dz, float* dzc, hipStream_t stream);
-hipError_t launch_dx_combine(int out_dtype, const float* dxr, const float* dxs, const int32_t* pos,
+// dx = dxs (if given) + the token's dispatched routed rows (fp16 when
+// row_dtype is 1, else fp32) + sum_j dzc_j bank_j, in fp32 in that order,
+// rounded once to out_dtype
+hipError_t launch_dx_combine(int row_dtype, int out_dtype, const void* dxr, const float* dxs, const int32_t* pos,
                              const int32_t* topk_idx, const float* dzc, const float* bank, void* dx, int T, int H,
                              int E, int S, int k, hipStream_t stream);
 // d bank = dz^T x (fp32), as kBankSplit token-range partials summed in order
