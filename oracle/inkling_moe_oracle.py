@@ -90,9 +90,10 @@ def log_sigmoid(z) -> np.ndarray:
 
 
 def selection_scores(z_routed, bias) -> np.ndarray:
-    """s[t, e] = sigma(z[t, e]) + b[e]  (InklingGate: sigmoid scores plus a
-    per-expert correction bias; InklingCorrectionBias.forward adds it in the
-    routing score dtype, fp64 here)."""
+    """s[t, e] = sigma(z[t, e]) + b[e]  (Inkling layers page, InklingGate: the
+    sigmoid of each routed logit shifted by expert e's own bias term;
+    InklingCorrectionBias.forward adds it in the routing score dtype, fp64
+    here)."""
     return sigmoid(z_routed) + _f64(bias)[None, :]
 
 
@@ -151,8 +152,8 @@ def permutation(topk_indices, n_routed: int, token_mask=None):
     slot = t * k + i.  counts[e] = number of slots routed to e; offsets =
     exclusive prefix sum (length E+1); sorted_slots lists the slots of expert 0,
     then expert 1, ..., each in ascending slot order.  Tokens whose mask entry
-    is True (padding) are left out (InklingMoE.forward: padded tokens are
-    excluded from routed-expert dispatch).
+    is True (padding) are left out (Inkling layers page, InklingMoE.forward:
+    masked tokens get no routed rows).
     Returns (counts int64 [E], offsets int64 [E+1], sorted_slots int64 [n]).
     """
     idx = np.asarray(topk_indices, dtype=np.int64)
@@ -259,9 +260,10 @@ def moe_forward(x, gate_bank, bias, w_gu, w_d, wsh_gu, wsh_d, top_k: int,
 # --------------------------------------------------------------------------
 
 def dense_mlp(x, w_gu, w_d, global_scale: float) -> np.ndarray:
-    """InklingDenseMLP.forward: the dense MLP over the fused interleaved
-    gate_up projection [2I, H] (row 2j gate_j, 2j+1 up_j), down projection
-    [H, I], and the module's global_scale parameter.  The page does not say
+    """InklingDenseMLP.forward (Inkling layers page): one SwiGLU MLP whose
+    gate and up weights sit interleaved in a single projection [2I, H] (row
+    2j gate_j, 2j+1 up_j), a down projection [H, I], and the module's
+    global_scale parameter.  The page does not say
     where global_scale enters; it is read as scaling the MLP output (equal in
     exact arithmetic to scaling the activation, since down_proj is linear)."""
     return float(global_scale) * expert_ffn(x, w_gu, w_d)
