@@ -4,8 +4,8 @@
 // Follows the Inkling layers page (nemo_automodel.components.models.inkling.layers),
 // InklingGate and InklingCorrectionBias: the gate bank holds the routed rows
 // followed by the shared rows; selection uses sigmoid(logit) + bias; the
-// returned weights are softmax(log sigmoid([selected routed || shared] logits))
-// scaled by route_scale * global_scale.
+// returned weights are route_scale * global_scale times
+// softmax(log sigmoid([selected routed || shared] logits)).
 //
 // Precision: the page fixes fp32 gate operands.  Logits are accumulated here in
 // fp64 from the exactly widened fp32 bank and bf16/fp32 hidden states, and

@@ -18,7 +18,7 @@ What it computes follows the Inkling layers page
   * InklingSharedExperts: always-on experts whose outputs are weighted by the
     shared gammas before summation.
   * InklingMoE.forward: routed + shared outputs summed, output shaped like the
-    input; padded tokens are excluded from routed dispatch.
+    input; masked tokens get no routed rows.
   * InklingDenseMLP: the dense SwiGLU MLP on the same interleaved layout,
     scaled by its global_scale parameter.
   * The backward of InklingMoE.forward: gradients of <dout, out> with respect
@@ -198,7 +198,7 @@ def expert_ffn(rows, w_gu, w_d, routing_weights=None) -> np.ndarray:
 
 def shared_experts(x, wsh_gu, wsh_d, gammas) -> np.ndarray:
     """InklingSharedExperts.forward: sum over s of gamma[:, s] * expert_s(x);
-    the gammas weight each expert's output before the summation."""
+    each shared expert's output is multiplied by its gamma, then added."""
     x = _f64(x)
     g = _f64(gammas)
     out = np.zeros((x.shape[0], _f64(wsh_d[0]).shape[0] if len(wsh_d) else x.shape[1]), dtype=F64)
