@@ -113,7 +113,7 @@ struct BwdActBufs {
 // their stored layout), then the SwiGLU backward: dh, a and partial
 // routing-weight gradients (round counters 16..23)
 hipError_t launch_dact(const MoeGemmParams& p, const BwdActBufs& b, hipStream_t stream);
-// dx rows = gate_up^T dh: routed dh_r -> dx_r [T*k][H] fp32 (slot rows),
+// dx rows = gate_up^T dh: routed dh_r -> dx_r [T*k][H] (slot rows; fp16 for bf16 layers, else fp32),
 // shared dh_sh [T][S*2I] -> dx_sh [T][H] fp32; the gate_up weights read in
 // their stored layout (round counters 8..15)
 hipError_t launch_dx(const MoeGemmParams& p, const void* dh_r, const void* dh_sh, void* dx_r, void* dx_sh,
