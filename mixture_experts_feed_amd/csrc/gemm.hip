@@ -1421,9 +1421,10 @@ constexpr int prefill_sched() {
 constexpr int kSyncMinRounds = 8;
 constexpr int kPrefillBN = 256;
 // weight gradients: 128 (N) x 256 (M) tiles of four waves, 64-byte K rows, two
-// workgroups per CU, so that one's fp32 stores overlap the other's K loop
-// (measured: 10.55 against 10.93 ms for the two launches of the prefill
-// backward, same bits)
+// workgroups per CU (measured: 10.55 against 10.93 ms for the two launches of
+// the prefill backward with 256 x 256 tiles, same bits).  Their fp32 stores
+// still do not overlap the K loops: the HBM write-back of the gradients costs
+// its full time with every tile shape, occupancy and start offset tried.
 constexpr int kWgradBN = 128, kWgradRowB = 64;
 constexpr int kDecodeBN = 128, kDecodeStages = 4, kDecodeRowB = 128, kDecodeGridPerCU = 1;
 int cfg_bn(int cfg) { return cfg == 0 ? kPrefillBN : kDecodeBN; }
