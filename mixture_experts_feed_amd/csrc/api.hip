@@ -159,7 +159,7 @@ int run_route(const inkling_moe_dims_t* d, const Layout& L, const void* x, const
         HIP_TRY(launch_build_masks(rb.topk_idx, pad, T, E, k, masks, L.W, s));
         HIP_TRY(launch_scan(masks, L.W, E, prefix, rb.counts, rb.offsets, rb.tiles ? L.bm : 0, rb.tiles, rb.num_tiles,
                             rc, s));
-        HIP_TRY(launch_scatter(rb.topk_idx, rb.topk_w, pad, masks, prefix, rb.offsets, T, E, k, L.W, rb.sorted_slots,
+        HIP_TRY(launch_scatter(rb.topk_idx, rb.topk_w, pad, masks, prefix, rb.offsets, T, k, L.W, rb.sorted_slots,
                                rb.row_token, rb.row_gamma, rb.pos, s));
     }
     HIP_TRY(mark(3, s));

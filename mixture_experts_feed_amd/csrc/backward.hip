@@ -143,8 +143,8 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const TR* __restrict__ 
                                                          const int32_t* __restrict__ pos,
                                                          const int32_t* __restrict__ topk_idx,
                                                          const float* __restrict__ dzc,
-                                                         const float* __restrict__ bank, TO* __restrict__ dx, int T,
-                                                         int H, int E, int S, int k) {
+                                                         const float* __restrict__ bank, TO* __restrict__ dx, int H,
+                                                         int E, int S, int k) {
     // one workgroup per token: its slots, experts and gate terms are uniform
     // (scalar loads)
     const int t = blockIdx.x, hq = H >> 2, nj = k + S;
@@ -199,13 +199,6 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const TR* __restrict__ 
     }
 }
 
-template <typename TX>
-__device__ __forceinline__ float to_f32(TX v);
-template <>
-__device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
-template <>
-__device__ __forceinline__ float to_f32<float>(float v) { return v; }
-
 constexpr int kBankSplit = 32;   // token ranges summed separately, then in order
 constexpr int kBankJW = 3;       // 16-row blocks of the bank per wave
 
@@ -229,7 +222,6 @@ __global__ __launch_bounds__(64) void dbank_partial_kernel(const float* __restri
     for (int u = 0; u < kBankJW; ++u)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[u][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
     for (int t = tb; t < te; t += 4) {
         const int tt = t + kr;
         const bool tv = tt < te;
@@ -329,8 +321,8 @@ hipError_t launch_dx_combine(int row_dtype, int out_dtype, const void* dxr, cons
         using TR = decltype(tr);
         using TO = decltype(to);
         hipLaunchKernelGGL((dx_combine_kernel<TR, TO>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const TR*>(dxr), dxs, pos, topk_idx, dzc, bank, static_cast<TO*>(dx), T, H, E,
-                           S, k);
+                           static_cast<const TR*>(dxr), dxs, pos, topk_idx, dzc, bank, static_cast<TO*>(dx), H, E, S,
+                           k);
     };
     if (row_dtype == 1) {
         if (out_dtype == 1) go(f16_t{}, bf16_t{});

@@ -215,10 +215,6 @@ __device__ __forceinline__ uint4 read_tr16_frag(const uint8_t* p, int row_bytes)
 template <typename TE>
 __device__ __forceinline__ void store2(TE* p, float a, float b);
 template <>
-__device__ __forceinline__ void store2<bf16_t>(bf16_t* p, float a, float b) {
-    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
-template <>
 __device__ __forceinline__ void store2<float>(float* p, float a, float b) {
     *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
@@ -263,16 +259,6 @@ __device__ __forceinline__ f32x4_t load4f<f16_t>(const f16_t* p) {
 
 template <typename TE>
 __device__ __forceinline__ void load8f(const TE* p, float* v);
-template <>
-__device__ __forceinline__ void load8f<bf16_t>(const bf16_t* p, float* v) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = __uint_as_float(w[j] << 16);
-        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-}
 template <>
 __device__ __forceinline__ void load8f<float>(const float* p, float* v) {
     const float4 a = *reinterpret_cast<const float4*>(p);

@@ -30,7 +30,7 @@ hipError_t launch_build_masks(const int32_t* topk_idx, const uint8_t* pad, int T
 hipError_t launch_scan(const uint64_t* masks, int W, int E, int32_t* prefix, int32_t* counts, int32_t* offsets,
                        int bm, RoutedTile* tiles, int32_t* num_tiles, int32_t* round_counters, hipStream_t stream);
 hipError_t launch_scatter(const int32_t* topk_idx, const float* topk_w, const uint8_t* pad, const uint64_t* masks,
-                          const int32_t* prefix, const int32_t* offsets, int T, int E, int k, int W,
+                          const int32_t* prefix, const int32_t* offsets, int T, int k, int W,
                           int32_t* sorted_slots, int32_t* row_token, float* row_gamma, int32_t* pos,
                           hipStream_t stream);
 // T <= 64: the three steps above in one launch (same outputs)

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
                                                      const uint8_t* __restrict__ pad,
                                                      const uint64_t* __restrict__ masks,
                                                      const int32_t* __restrict__ prefix,
-                                                     const int32_t* __restrict__ offsets, int T, int E, int k, int W,
+                                                     const int32_t* __restrict__ offsets, int T, int k, int W,
                                                      int32_t* __restrict__ sorted_slots,
                                                      int32_t* __restrict__ row_token, float* __restrict__ row_gamma,
                                                      int32_t* __restrict__ pos) {
@@ -238,11 +238,11 @@ hipError_t launch_scan(const uint64_t* masks, int W, int E, int32_t* prefix, int
 }
 
 hipError_t launch_scatter(const int32_t* topk_idx, const float* topk_w, const uint8_t* pad, const uint64_t* masks,
-                          const int32_t* prefix, const int32_t* offsets, int T, int E, int k, int W,
+                          const int32_t* prefix, const int32_t* offsets, int T, int k, int W,
                           int32_t* sorted_slots, int32_t* row_token, float* row_gamma, int32_t* pos,
                           hipStream_t stream) {
     hipLaunchKernelGGL(scatter_kernel, dim3(W), dim3(64), 0, stream, topk_idx, topk_w, pad, masks, prefix, offsets, T,
-                       E, k, W, sorted_slots, row_token, row_gamma, pos);
+                       k, W, sorted_slots, row_token, row_gamma, pos);
     return hipGetLastError();
 }
 
