@@ -161,8 +161,8 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
  * library's load on that GPU until the process ends; the call allocates and
  * frees nothing.  Returns INKLING_ERR_TOO_LARGE, before anything is enqueued,
  * when inkling_moe_workspace_size() for these dims exceeds that size (at
- * hidden 6144, top-8, 2 shared experts, intermediate 2048 that is above 429
- * tokens; decode batches of 32 tokens need 5 MB).  Every call on one GPU uses that GPU's one array, and the
+ * hidden 6144, top-8, 2 shared experts, intermediate 2048 that is above 371
+ * tokens; decode batches of 32 tokens need 5.8 MB).  Every call on one GPU uses that GPU's one array, and the
  * array keeps what the last call left there: calls that overlap in time on
  * one GPU (other streams, other threads) race and must be ordered on one
  * stream.  The device is the calling thread's current HIP device.
