@@ -56,6 +56,33 @@ def _draw_cases(n=10, seed=20261203):
 CASES = _draw_cases()
 
 
+def _draw_wide_cases(n=14, seed=202):
+    """Wider ranges than _draw_cases: E up to 256 (past one wave of experts per
+    lane), k up to 12, S up to 4, hidden up to 1024, intermediate up to 512,
+    token counts at and around the tile and word boundaries (1, 7, 63-65, 255,
+    257, 2047, 2049, 4100), masks that pad some or every token."""
+    rng = np.random.default_rng(seed)
+    cases = {}
+    for c in range(n):
+        E = int(rng.choice([1, 3, 8, 17, 64, 130, 256]))
+        k = int(rng.integers(1, min(E, 12) + 1))
+        S = int(rng.integers(0, 5))
+        kw = dict(T=int(rng.choice([1, 7, 63, 64, 65, 255, 257, 1000, 2047, 2049, 4100])),
+                  hidden=64 * int(rng.integers(1, 17)), n_routed=E, top_k=k, n_shared=S,
+                  intermediate=64 * int(rng.integers(1, 9)),
+                  dtype="f32" if rng.random() < 0.25 else "bf16",
+                  route_scale=float(rng.choice([1.0, 2.5, 8.0])),
+                  gate_dist=("uniform", 0.05), bias_dist=("uniform", 0.05))
+        mask_frac = float(rng.choice([0.0, 0.0, 0.3, 1.0]))
+        name = (f"w{c}_T{kw['T']}_H{kw['hidden']}_E{E}_k{k}_S{S}_I{kw['intermediate']}_{kw['dtype']}"
+                f"{'_pad' if mask_frac else ''}")
+        cases[name] = (wl.custom(name=name, **kw), mask_frac)
+    return cases
+
+
+WIDE = _draw_wide_cases()
+
+
 def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -113,3 +140,35 @@ def test_random_shape_saved_backward(name):
         g = torch.Generator().manual_seed(w.T)
         mask = (torch.rand((w.T,), generator=g) < mask_frac).to(torch.uint8).to(DEV)
     saved_vs_recompute(name, w, mask)
+
+
+@pytest.mark.parametrize("name", list(WIDE))
+def test_wide_random_shape(name):
+    """Forward parity on the wider draw; the backward too where the oracle's
+    backward stays quick (T <= 2100, hidden <= 512)."""
+    w, mask_frac = WIDE[name]
+    _say(f"[wide] {name}")
+    inp = wl.make_inputs(w, device=DEV)
+    mask = None
+    if mask_frac > 0:
+        g = torch.Generator().manual_seed(w.T + 1)
+        mask = (torch.rand((w.T,), generator=g) < mask_frac).to(torch.uint8).to(DEV)
+    S = w.n_shared
+    out, routing = B.forward(inp["x"], inp["gate_bank"], inp["bias"], inp["w_gu"], inp["w_d"],
+                             inp["wsh_gu"] if S else None, inp["wsh_d"] if S else None, w.top_k,
+                             inp["route_scale"], inp["global_scale"], padding_mask=mask,
+                             return_routing=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = P.oracle_route(inp, w.top_k, mask)
+    band = P.check_routing(routing, ref, w.top_k)
+    pm = None if mask is None else mask.cpu().numpy().astype(bool)
+    o_ref, _ = oracle.moe_forward(P.host(inp["x"]), P.host(inp["gate_bank"]), P.host(inp["bias"]),
+                                  P.HostExperts(inp["w_gu"]), P.HostExperts(inp["w_d"]),
+                                  P.HostExperts(inp["wsh_gu"] if S else None),
+                                  P.HostExperts(inp["wsh_d"] if S else None),
+                                  w.top_k, w.route_scale, w.global_scale, padding_mask=pm, routing=ref)
+    rel = P.check_output(out, o_ref, w.dtype)
+    _say(f"[wide] forward ok: band={band} max_err/rms={rel:.2e}")
+    if w.T <= 2100 and w.hidden <= 512:
+        from tests.test_gpu_backward import _full_backward
+        _full_backward(w, padding_mask=mask)
