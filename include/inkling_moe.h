@@ -14,7 +14,7 @@
  *                      output, the activated output scaled by the routing weight.
  *   InklingSharedExperts  always-on experts weighted by the shared gammas.
  *   InklingMoE.forward routed + shared outputs summed; output shaped like the
- *                      input; padded tokens excluded from routed dispatch.
+ *                      input; masked (padded) tokens get no routed rows.
  *
  * Readings where the page is silent: equal selection scores go to the lower
  * expert index and topk_* are ordered by descending score; route_scale *
@@ -144,9 +144,10 @@ int inkling_moe_route(const inkling_moe_dims_t* dims, const void* x, const inkli
  * Precision: products accumulate in fp32; the expert outputs are summed in
  * fp32 in a fixed order and rounded once, so the result is bit-reproducible.
  * With dtype INKLING_BF16 the activation between an expert's two projections,
- * gamma * silu(gate) * up, is rounded to fp16 (nearest even), and the bf16
- * down weights are taken as fp16, which is exact for 2^-17 <= |w| < 2^16;
- * the activation must stay below 65504 in magnitude (above it is inf). */
+ * gamma * silu(gate) * up, is rounded to fp16 (nearest even), the bf16 down
+ * weights are taken as fp16, which is exact for 2^-17 <= |w| < 2^16, and each
+ * routed expert's output row is rounded to fp16 before the fp32 sum; both
+ * intermediates must stay below 65504 in magnitude (above it they are inf). */
 int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
                         const inkling_experts_t* experts, const uint8_t* padding_mask, void* out,
                         inkling_route_out_t* route_out, void* workspace, size_t workspace_bytes,
@@ -162,10 +163,11 @@ int inkling_moe_forward(const inkling_moe_dims_t* dims, const void* x, const ink
  * frees nothing.  Returns INKLING_ERR_TOO_LARGE, before anything is enqueued,
  * when inkling_moe_workspace_size() for these dims exceeds that size (at
  * hidden 6144, top-8, 2 shared experts, intermediate 2048 that is above 371
- * tokens; decode batches of 32 tokens need 5.8 MB).  Every call on one GPU uses that GPU's one array, and the
- * array keeps what the last call left there: calls that overlap in time on
- * one GPU (other streams, other threads) race and must be ordered on one
- * stream.  The device is the calling thread's current HIP device.
+ * tokens; decode batches of 32 tokens need 5.8 MB).  Every call on one GPU
+ * uses that GPU's one array, and the array keeps what the last call left
+ * there: calls that overlap in time on one GPU (other streams, other threads)
+ * race and must be ordered on one stream.  The device is the calling thread's
+ * current HIP device.
  */
 #define INKLING_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int inkling_moe_forward_noalloc(const inkling_moe_dims_t* dims, const void* x, const inkling_gate_t* gate,
@@ -242,7 +244,8 @@ int inkling_moe_backward(const inkling_moe_dims_t* dims, const void* x, const in
  *   gate_j, 2j+1 = up_j;  down [hidden][intermediate];  out [T][hidden]
  *   (out_dtype; INKLING_F32 keeps the fp32 result unrounded), must not alias x.
  * Same conventions and errors as inkling_moe_forward; limits hidden % 64 == 0,
- * intermediate % 64 == 0.
+ * intermediate % 64 == 0.  With dtype INKLING_BF16 the activation is rounded
+ * to fp16 and the down weights are taken as fp16, as in inkling_moe_forward.
  */
 typedef struct {
     int64_t T;
